@@ -1,0 +1,316 @@
+"""CPU oracle for the AWQ per-layer search path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the package's smoke check and the benchmark's CPU
+baseline leg may import this module.  The product path never calls it: it is
+the plain, slow, obviously correct statement of what the GPU path computes,
+written from the pages and sharing no code with the HIP kernels.
+
+Sources (cited by page title and section):
+  [P1] dev.to, "AWQ: How Activation-Aware Quantization Saves 4-bit LLMs"
+       - "How does AWQ decide which weights to protect?" (channel_importance listing)
+       - "How does AWQ protect channels without mixed precision?" (search_scale listing)
+       - "What do you actually deploy" (quant_config: zero point, group 128, 4 bit)
+  [P2] esaholic.com, "What is AWQ Quantization?", pipeline step
+       "INT4 Weight Packing & Export" (codes packed into INT32 containers)
+  [P3] modelrefs.com, "AWQ (Activation-Aware Weight Quantization) -- AI Glossary",
+       "Example: Where 4-bit memory saving comes from"
+  [P4] mbrenndoerfer.com, "AWQ > Salient Weight Preservation",
+       step-size equation s_q = (w_max - w_min)/(2^b - 1) and the scaling identity
+  [P5] mbrenndoerfer.com, "AWQ > Summary", "Salient weight identification",
+       "The scaling formula"
+
+Precision (the pages fix none of it, so these are readings):
+  * element-wise quantizer arithmetic is IEEE binary32 with round-to-nearest-
+    even, as numpy float32 performs it: the integer codes are decided in the
+    same precision the kernels use;
+  * sums and contractions are binary64 (exact products of fp16 inputs);
+  * the dequantized weight is rounded once to fp16 from the exact product of
+    the binary32 value (q - z) * step and the binary32 reciprocal of s.
+
+Every function here is pinned by tests that do not re-use its own formulas:
+worked examples built on the quantization grid, exact rational brute force,
+closed forms on Hadamard inputs, invariances and the page's memory
+arithmetic.  The one result with no external pin is the absolute value of the
+losses on the large synthetic configurations (parity there is GPU vs. this
+oracle only).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+F16, F32, F64 = np.float16, np.float32, np.float64
+
+#: default search settings: quant_config of [P1] "What do you actually deploy"
+#: (zero point on, group 128, 4 bit) and the grid size and floor of the
+#: search_scale listing in [P1] "How does AWQ protect channels".
+W_BIT = 4
+GROUP = 128
+N_GRID = 20
+SAL_FLOOR = F32(1e-4)
+
+
+class NonFiniteLosses(ArithmeticError):
+    """No grid point produced a finite loss (the listing then keeps no scale)."""
+
+
+# --------------------------------------------------------------------------
+# step 1: activation saliency
+# --------------------------------------------------------------------------
+def act_stats(X: np.ndarray) -> np.ndarray:
+    """Per-input-channel saliency: the mean of |X[t, k]| over calibration tokens.
+
+    [P1] channel_importance listing (abs, then mean over the token axis);
+    [P5] "Salient weight identification" (average absolute activation).
+
+    The sum is exact: |x| of an fp16 value is an integer multiple of 2^-24, so
+    summing those integers is exact for any token count.  The mean is then the
+    binary64 quotient, rounded to binary32.
+    """
+    X = np.asarray(X)
+    if X.dtype != F16 or X.ndim != 2:
+        raise TypeError("X must be a 2-D float16 array [tokens, in_features]")
+    n = X.shape[0]
+    units = (np.abs(X).astype(F64) * 2.0 ** 24).astype(np.int64)   # exact integers
+    total = units.sum(axis=0, dtype=np.int64)                      # exact
+    mean = total.astype(F64) * 2.0 ** -24 / F64(n)
+    return mean.astype(F32)
+
+
+# --------------------------------------------------------------------------
+# step 2: per-channel scales for every grid point
+# --------------------------------------------------------------------------
+def alphas(n_grid: int = N_GRID) -> np.ndarray:
+    """alpha_i = i / n_grid for i = 0 .. n_grid-1 ([P1] search_scale listing:
+    0 means no scaling; the grid stops one point short of 1)."""
+    return np.arange(n_grid, dtype=F64) / F64(n_grid)
+
+
+def scale_table(sal: np.ndarray, n_grid: int = N_GRID, floor: float = SAL_FLOOR):
+    """s[i, k] = max(sal_k, floor) ** alpha_i and its reciprocal.
+
+    [P1] search_scale listing: the saliency is clamped from below at 1e-4 and
+    raised to alpha; [P5] "The scaling formula".  The power is taken in
+    binary64 and rounded to binary32; the reciprocal is a binary32 division.
+    """
+    sal = np.asarray(sal, dtype=F32)
+    base = np.maximum(sal, F32(floor)).astype(F64)
+    s = np.power(base[None, :], alphas(n_grid)[:, None]).astype(F32)
+    inv_s = (F32(1.0) / s).astype(F32)
+    return s, inv_s
+
+
+# --------------------------------------------------------------------------
+# step 3: asymmetric group quantization of W * diag(s)
+# --------------------------------------------------------------------------
+@dataclass
+class GroupQuant:
+    step: np.ndarray   # [rows, n_groups] float32
+    zero: np.ndarray   # [rows, n_groups] float32 (an integer value, +0 for zero)
+    q: np.ndarray      # [rows, in] uint8 codes in 0 .. 2^b-1
+    tie: np.ndarray    # [rows, in] bool: pre-round value within 1 ulp of a .5 tie
+
+
+def _near_half(x: np.ndarray) -> np.ndarray:
+    """True where x lies within one binary32 ulp of a half-integer."""
+    frac = np.abs(x.astype(F64) - (np.floor(x.astype(F64)) + 0.5))
+    return frac <= np.spacing(np.abs(x).astype(F32)).astype(F64)
+
+
+def quantize(ws: np.ndarray, group: int = GROUP, w_bit: int = W_BIT) -> GroupQuant:
+    """Quantize binary32 rows group-wise to asymmetric w_bit integers.
+
+    [P4] step-size equation: step = (max - min) / (2^b - 1) over a group;
+    [P1] quant_config: zero point on, groups of 128 along in_features;
+    [P3] "How it works", step 4: every group has its own scale.
+
+    Per group (binary32, round half to even):
+        step = (mx - mn) / 15          (a zero range takes step = 1)
+        zero = rint(-mn / step)        (not clamped; -0 becomes +0)
+        q    = clamp(rint(w / step) + zero, 0, 15)
+    """
+    ws = np.asarray(ws)
+    if ws.dtype != F32 or ws.ndim != 2 or ws.shape[1] % group:
+        raise TypeError("ws must be float32 [rows, in] with in a multiple of the group")
+    rows, k = ws.shape
+    qmax = F32(2 ** w_bit - 1)
+    g = ws.reshape(rows, k // group, group)
+    mn = g.min(axis=2)
+    mx = g.max(axis=2)
+    step = ((mx - mn) / qmax).astype(F32)
+    step = np.where(step == F32(0), F32(1), step).astype(F32)
+    zpre = (-mn / step).astype(F32)
+    zero = (np.rint(zpre) + F32(0)).astype(F32)
+    x = (g / step[:, :, None]).astype(F32)
+    q = np.clip(np.rint(x) + zero[:, :, None], F32(0), qmax).astype(F32)
+    tie = _near_half(x) | _near_half(zpre)[:, :, None]
+    return GroupQuant(step, zero, q.reshape(rows, k).astype(np.uint8),
+                      tie.reshape(rows, k))
+
+
+def scaled_weights(W: np.ndarray, s_row: np.ndarray) -> np.ndarray:
+    """W * diag(s) in binary32 (fp16 weights are exact in binary32).
+
+    [P1] search_scale listing: weight columns are multiplied by s before
+    quantizing; [P4] scaling identity: column j of W is multiplied by s_j."""
+    return (np.asarray(W, dtype=F16).astype(F32) * np.asarray(s_row, dtype=F32)[None, :]).astype(F32)
+
+
+# --------------------------------------------------------------------------
+# step 4: dequantize and divide by s
+# --------------------------------------------------------------------------
+def dequantize(gq: GroupQuant, inv_s_row: np.ndarray, group: int = GROUP,
+               literal_div: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp16 weight of the quantized, unscaled layer.
+
+    [P1] search_scale listing: the quantized scaled weight is divided by s
+    ("fold s back"); [P2] "Technical Architecture": Q(W s) s^-1.
+
+    t = binary32((q - zero) * step); the result is t times the binary32
+    reciprocal of s, rounded once to fp16 (the product of two binary32 values
+    is exact in binary64).  ``literal_div`` (the s row) divides by s instead,
+    to measure what the reciprocal changes.
+    """
+    rows, k = gq.q.shape
+    ng = k // group
+    step = np.repeat(gq.step, group, axis=1)
+    zero = np.repeat(gq.zero, group, axis=1)
+    t = ((gq.q.astype(F32) - zero) * step).astype(F32)
+    if literal_div is not None:
+        return (t.astype(F64) / np.asarray(literal_div, F32).astype(F64)[None, :]).astype(F16)
+    prod = t.astype(F64) * np.asarray(inv_s_row, dtype=F32).astype(F64)[None, :]
+    return prod.astype(F16)
+
+
+def fake_quant(W: np.ndarray, s_row: np.ndarray, inv_s_row: np.ndarray,
+               group: int = GROUP, w_bit: int = W_BIT) -> np.ndarray:
+    """Q(W diag(s)) diag(s)^-1 as fp16 (steps 3 and 4 together)."""
+    return dequantize(quantize(scaled_weights(W, s_row), group, w_bit), inv_s_row, group)
+
+
+# --------------------------------------------------------------------------
+# step 5: output error, argmin over the grid
+# --------------------------------------------------------------------------
+def output_mse(X: np.ndarray, W: np.ndarray, Wq: np.ndarray) -> float:
+    """mean over tokens and outputs of (X Wq^T - X W^T)^2, in binary64.
+
+    [P1] search_scale listing: the error is the mean of the squared difference
+    between the quantized layer's output and the fp16 layer's output.  The
+    reference output is not rounded (fp16 inputs, exact binary64 products).
+    """
+    X64 = np.asarray(X, F16).astype(F64)
+    y_ref = X64 @ np.asarray(W, F16).astype(F64).T
+    y = X64 @ np.asarray(Wq, F16).astype(F64).T
+    d = y - y_ref
+    return float(np.mean(d * d))
+
+
+def argmin_first(losses: np.ndarray) -> int:
+    """Lowest grid index attaining the minimum finite loss.
+
+    [P1] search_scale listing: the best error starts at +inf and is replaced
+    only on a strictly smaller error, so the first minimum wins and a NaN
+    never wins.  No finite loss means no scale is chosen (raised here).
+    """
+    best, best_i = np.inf, -1
+    for i, v in enumerate(np.asarray(losses, dtype=F64)):
+        if v < best:
+            best, best_i = v, i
+    if best_i < 0:
+        raise NonFiniteLosses("no finite loss on the grid")
+    return best_i
+
+
+@dataclass
+class SearchResult:
+    losses: np.ndarray      # [n_grid] float64
+    best: int               # argmin index
+    s_best: np.ndarray      # [in] float32
+    s: np.ndarray           # [n_grid, in] float32
+    inv_s: np.ndarray       # [n_grid, in] float32
+
+
+def search_layer(X: np.ndarray, W: np.ndarray, sal: np.ndarray, n_grid: int = N_GRID,
+                 floor: float = SAL_FLOOR, group: int = GROUP, w_bit: int = W_BIT) -> SearchResult:
+    """The per-layer grid search, in the order of [P1]'s search_scale listing:
+    reference output; for each alpha: scale, quantize, fold back, output MSE;
+    keep the first strict minimum."""
+    s, inv_s = scale_table(sal, n_grid, floor)
+    X64 = np.asarray(X, F16).astype(F64)
+    y_ref = X64 @ np.asarray(W, F16).astype(F64).T
+    losses = np.empty(n_grid, dtype=F64)
+    for i in range(n_grid):
+        wq = fake_quant(W, s[i], inv_s[i], group, w_bit)
+        d = X64 @ wq.astype(F64).T - y_ref
+        losses[i] = np.mean(d * d)
+    best = argmin_first(losses)
+    return SearchResult(losses, best, s[best].copy(), s, inv_s)
+
+
+def tile_sq_error(X: np.ndarray, W: np.ndarray, s_row: np.ndarray, inv_s_row: np.ndarray,
+                  rows: slice, cols: slice, group: int = GROUP, w_bit: int = W_BIT) -> float:
+    """Sum of squared output differences over a token range x output range.
+
+    The same quantity as output_mse restricted to a sub-block (not divided by
+    its size): a large layer's loss is the sum of such blocks, which lets a
+    test check a large run one block at a time.
+    """
+    Wsub = np.asarray(W, F16)[cols]
+    wq = fake_quant(Wsub, s_row, inv_s_row, group, w_bit)
+    X64 = np.asarray(X, F16)[rows].astype(F64)
+    d = X64 @ wq.astype(F64).T - X64 @ Wsub.astype(F64).T
+    return float(np.sum(d * d))
+
+
+# --------------------------------------------------------------------------
+# packing the chosen codes
+# --------------------------------------------------------------------------
+@dataclass
+class Packed:
+    qweight: np.ndarray   # [out, in/8] int32, nibble j of word w = code of column 8w+j
+    step16: np.ndarray    # [out, in/group] float16
+    zero16: np.ndarray    # [out, in/group] float16
+    q: np.ndarray         # [out, in] uint8 (unpacked codes)
+    tie: np.ndarray       # [out, in] bool
+
+
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """Eight 4-bit codes per 32-bit word along in_features, lowest column in
+    the lowest nibble ([P2] pipeline step "INT4 Weight Packing & Export":
+    INT4 codes live in INT32 containers; the nibble order is our reading)."""
+    q = np.asarray(q, dtype=np.uint32)
+    rows, k = q.shape
+    q = q.reshape(rows, k // 8, 8)
+    word = np.zeros((rows, k // 8), dtype=np.uint32)
+    for j in range(8):
+        word |= (q[:, :, j] & np.uint32(0xF)) << np.uint32(4 * j)
+    return word.view(np.int32)
+
+
+def unpack_codes(qweight: np.ndarray) -> np.ndarray:
+    w = np.asarray(qweight).view(np.uint32)
+    rows, kw = w.shape
+    out = np.empty((rows, kw, 8), dtype=np.uint8)
+    for j in range(8):
+        out[:, :, j] = (w >> np.uint32(4 * j)) & np.uint32(0xF)
+    return out.reshape(rows, kw * 8)
+
+
+def pack(W: np.ndarray, s_row: np.ndarray, group: int = GROUP, w_bit: int = W_BIT) -> Packed:
+    """Quantize W diag(s) with exact division and pack the codes, with the
+    per-group step and zero point stored as fp16 ([P1] quant_config;
+    [P3] worked example: one 16-bit scale per 128 weights)."""
+    gq = quantize(scaled_weights(W, s_row), group, w_bit)
+    return Packed(pack_codes(gq.q), gq.step.astype(F16), gq.zero.astype(F16), gq.q, gq.tie)
+
+
+def packed_bytes(n_weights: int, group: int = GROUP, w_bit: int = W_BIT) -> dict:
+    """Storage of the packed format for n_weights weights (codes, steps, zeros)."""
+    return {
+        "codes": n_weights * w_bit // 8,
+        "steps": n_weights // group * 2,
+        "zeros": n_weights // group * 2,
+        "fp16": n_weights * 2,
+    }

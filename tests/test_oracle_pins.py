@@ -1,0 +1,393 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+None of these re-types the oracle's own formulas: expected values come from
+the pages' worked examples, exact rational brute force (tests/brute.py),
+closed forms on Hadamard inputs, invariances, and hand-built inputs whose
+quantization is exact by construction.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import brute
+import synth
+from oracle import awq_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+F16, F32, F64 = np.float16, np.float32, np.float64
+
+
+def hadamard(n):
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+# --------------------------------------------------------------- step formula
+def test_step_equation_worked_example():
+    """Step-size equation of 'AWQ > Salient Weight Preservation' on a group
+    whose values are all on the 1/16 grid (fixture derivation)."""
+    g = json.load(open(os.path.join(GOLD, "step_equation_example.json")))
+    u = np.array(g["u"], dtype=np.int64)
+    w = (u / 16.0).astype(F16)[None, :]
+    packed = O.pack(w, np.ones(128, F32))
+    assert float(packed.step16[0, 0]) == g["expected_step"]
+    assert float(packed.zero16[0, 0]) == g["expected_zero"]
+    assert np.array_equal(packed.q[0].astype(np.int64), u + g["expected_code_offset"])
+    # dequantization of exact codes returns the weights exactly
+    wq = O.fake_quant(w, np.ones(128, F32), np.ones(128, F32))
+    assert np.array_equal(wq.view(np.uint16), w.view(np.uint16))
+
+
+def test_memory_arithmetic_13b():
+    """Worked memory example of the modelrefs glossary page."""
+    g = json.load(open(os.path.join(GOLD, "memory_13b.json")))
+    b = O.packed_bytes(int(g["n_params"]), group=g["group_size"])
+    assert b["fp16"] / 1e9 == pytest.approx(g["fp16_gb"], rel=1e-12)
+    assert b["codes"] / 1e9 == pytest.approx(g["int4_gb"], rel=1e-12)
+    assert b["steps"] / 1e9 == pytest.approx(g["scales_gb_approx"], rel=g["rel_tol_approx"])
+    assert (b["codes"] + b["steps"]) / 1e9 == pytest.approx(g["total_gb_approx"],
+                                                            rel=g["rel_tol_approx"])
+    # zero points add the same again as the steps (not counted by the page)
+    assert b["zeros"] == b["steps"]
+    # the oracle's packed arrays have exactly these sizes
+    rng = np.random.default_rng(0)
+    W = rng.standard_normal((16, 256)).astype(F16)
+    p = O.pack(W, np.ones(256, F32))
+    bb = O.packed_bytes(W.size)
+    assert p.qweight.nbytes == bb["codes"] and p.step16.nbytes == bb["steps"]
+    assert p.zero16.nbytes == bb["zeros"]
+
+
+# ------------------------------------------------ brute force on tiny inputs
+def _tiny_case(seed, n=6, k=128, out=3):
+    _, X, W = synth.make_custom(n, k, out, seed)
+    return X, W
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_quantizer_matches_exact_rational_emulation(seed):
+    X, W = _tiny_case(seed, k=256, out=4)
+    sal = O.act_stats(X)
+    s, inv_s = O.scale_table(sal)
+    for i in (0, 7, 19):
+        gq = O.quantize(O.scaled_weights(W, s[i]))
+        wq = O.dequantize(gq, inv_s[i])
+        s_fr = [Fraction(float(v)) for v in s[i]]
+        for r in range(W.shape[0]):
+            bw, bq = brute.fake_quant_row([Fraction(float(v)) for v in W[r]], s_fr)
+            assert bq == gq.q[r].tolist()
+            assert [Fraction(float(v)) for v in wq[r]] == bw
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_losses_match_exact_rationals(seed):
+    X, W = _tiny_case(seed, n=5, k=128, out=3)
+    sal = O.act_stats(X)
+    res = O.search_layer(X, W, sal)
+    Xf = [[Fraction(float(v)) for v in row] for row in X]
+    Wf = [[Fraction(float(v)) for v in row] for row in W]
+    for i in (0, 5, 13, 19):
+        s_fr = [Fraction(float(v)) for v in res.s[i]]
+        Wq = [brute.fake_quant_row(row, s_fr)[0] for row in Wf]
+        exact = brute.mse_exact(Xf, Wf, Wq)
+        assert res.losses[i] == pytest.approx(float(exact), rel=1e-12, abs=0)
+
+
+def test_stats_exact_mean_then_two_roundings():
+    rng = np.random.default_rng(7)
+    X = (rng.standard_normal((37, 64)) * 50).astype(F16)
+    X[0, :4] = [F16(65504.0), F16(-65504.0), F16(2.0 ** -24), F16(-(2.0 ** -20))]
+    X[1, 4] = F16(0.0)
+    sal = O.act_stats(X)
+    for k in range(X.shape[1]):
+        m = brute.mean_abs_exact([Fraction(float(v)) for v in X[:, k]])
+        want = brute.round_rne(brute.round_rne(m, brute.BINARY64), brute.BINARY32)
+        assert Fraction(float(sal[k])) == want
+
+
+def test_stats_statistical_sanity():
+    """Non-outlier channels of N(0,1) activations: E|x| = sqrt(2/pi)."""
+    spec, X, _ = synth.make_layer(1)
+    sal = O.act_stats(X)
+    med = float(np.median(sal))
+    assert med == pytest.approx(math.sqrt(2 / math.pi), abs=0.03)
+    # the outlier channels are exactly the large ones
+    assert int((sal > 5).sum()) == spec.n_outliers
+
+
+def test_scale_table_against_high_precision_pow():
+    rng = np.random.default_rng(11)
+    sal = np.concatenate([rng.uniform(1e-6, 120, 24), [0.0, 1e-4, 1.0, 2.0]]).astype(F32)
+    s, inv_s = O.scale_table(sal)
+    floor = Fraction(float(F32(1e-4)))
+    for k, v in enumerate(sal):
+        base = max(Fraction(float(v)), floor)
+        for i in range(20):
+            exact = brute.pow_decimal(base, Fraction(i, 20))
+            want = brute.round_rne(brute.round_rne(exact, brute.BINARY64), brute.BINARY32)
+            assert Fraction(float(s[i, k])) == want, (k, i)
+            assert Fraction(float(inv_s[i, k])) == brute.round_rne(1 / want)
+    assert np.all(s[0] == 1) and np.all(inv_s[0] == 1)
+
+
+# ------------------------------------------------------ special cases / RTN
+def test_alpha_zero_is_plain_rtn():
+    """alpha = 0 means no scaling (search_scale listing), so grid point 0 must be
+    plain round-to-nearest group quantization of W, brute-forced without s."""
+    X, W = _tiny_case(5, n=4, k=256, out=3)
+    res = O.search_layer(X, W, O.act_stats(X))
+    assert np.all(res.s[0] == 1)
+    gq = O.quantize(O.scaled_weights(W, res.s[0]))
+    Xf = [[Fraction(float(v)) for v in row] for row in X]
+    Wf = [[Fraction(float(v)) for v in row] for row in W]
+    Wq_rtn = []
+    for r, row in enumerate(Wf):
+        codes, deq = [], []
+        for g0 in range(0, 256, 128):
+            step, zero, q = brute.quantize_group(row[g0:g0 + 128])
+            codes += q
+            deq += [brute.round_rne(brute.round_rne((qq - zero) * step), brute.BINARY16) for qq in q]
+        assert codes == gq.q[r].tolist()
+        Wq_rtn.append(deq)
+    assert res.losses[0] == pytest.approx(float(brute.mse_exact(Xf, Wf, Wq_rtn)), rel=1e-12)
+
+
+def _grid_layer(rows, k, rng, s_pow2):
+    """W whose scaled groups lie exactly on their own quantization grid."""
+    W = np.empty((rows, k), dtype=F64)
+    codes = np.empty((rows, k), dtype=np.int64)
+    for r in range(rows):
+        for g0 in range(0, k, 128):
+            c = rng.integers(0, 16, 128)
+            c[rng.integers(0, 128)] = 0
+            c[(rng.integers(0, 127) + 1 + np.argmin(c)) % 128] = 15
+            z = int(rng.integers(1, 15))
+            step = 2.0 ** -int(rng.integers(6, 10))
+            ws = (c - z) * step
+            W[r, g0:g0 + 128] = ws / s_pow2[g0:g0 + 128]
+            codes[r, g0:g0 + 128] = c
+    Wh = W.astype(F16)
+    assert np.array_equal(Wh.astype(F64), W)          # exactly representable
+    return Wh, codes
+
+
+def test_scaling_identity_is_exact_when_rounding_is_exact():
+    """Scaling identity of 'AWQ > Salient Weight Preservation': scaling a
+    column by s and dividing it back cancels exactly; with power-of-two s and
+    groups on their grid nothing rounds, so the codes are the construction,
+    the dequantized weight is W bit for bit and the loss is zero."""
+    rng = np.random.default_rng(3)
+    k = 256
+    s = (2.0 ** rng.integers(-2, 3, k)).astype(F32)
+    W, codes = _grid_layer(4, k, rng, s.astype(F64))
+    p = O.pack(W, s)
+    assert np.array_equal(p.q.astype(np.int64), codes)
+    wq = O.fake_quant(W, s, (F32(1) / s).astype(F32))
+    assert np.array_equal(wq.view(np.uint16), W.view(np.uint16))
+    X = (rng.standard_normal((8, k))).astype(F16)
+    assert O.output_mse(X, W, wq) == 0.0
+
+
+def test_zero_range_group():
+    W = np.zeros((2, 128), F16)
+    W[1] = F16(0.375)
+    p = O.pack(W, np.ones(128, F32))
+    assert np.all(p.step16 == 1)
+    assert p.zero16[0, 0] == 0 and not np.signbit(p.zero16[0, 0])
+    wq = O.fake_quant(W, np.ones(128, F32), np.ones(128, F32))
+    assert np.array_equal(wq[0], W[0])
+
+
+# ------------------------------------------------ closed form: single outlier
+def _single_outlier_case(out=4):
+    n = k = 128
+    j = 37
+    X = hadamard(n)
+    X[:, j] *= 2.0
+    X = X.astype(F16)
+    base = np.tile(np.array([-5, 10] + [0] * 126, dtype=F64) / 16.0, (out, 1))
+    rng = np.random.default_rng(1)
+    base[:, 2:] = rng.integers(-5, 11, (out, 126)) / 16.0
+    base[:, j] = 0.0
+    u0 = np.array([129, 130, 131, 132][:out], dtype=F64) / 256.0
+    W = base.copy()
+    W[:, j] = u0 / 16.0
+    return X, W.astype(F16), u0, j
+
+
+def test_single_outlier_loss_closed_form_and_monotone():
+    """Hadamard activations with one channel doubled: X^T X is diagonal, the
+    loss separates per weight, and only the outlier weight has error.  Scaling
+    it by 2^alpha shrinks that error ('How does AWQ protect channels', the
+    1/s argument), so the loss decreases strictly along the grid and follows
+    (2^-alpha - u0)^2 / 64 per row."""
+    X, W, u0, j = _single_outlier_case()
+    sal = O.act_stats(X)
+    assert sal[j] == 2 and np.all(np.delete(sal, j) == 1)
+    res = O.search_layer(X, W, sal)
+    assert np.all(np.diff(res.losses) < 0)
+    assert res.best == 19
+    for i, a in enumerate(O.alphas()):
+        e = (2.0 ** -a - u0) / 16.0                 # exact outlier weight error
+        delta = 2.0 ** -16                          # fp16 half-ulp on [1/32, 1/16)
+        closed = np.mean(4 * e * e)
+        bound = np.mean(4 * (2 * np.abs(e) * delta + delta * delta))
+        assert abs(res.losses[i] - closed) <= bound + 1e-15
+    assert res.losses[0] == pytest.approx(np.mean((1 - u0) ** 2 / 64), rel=1e-9)
+
+
+def test_all_equal_saliency_ties_choose_first():
+    """|x| = 1 everywhere gives s = 1 for every alpha: identical losses, and the
+    strict comparison of the search keeps the first grid point."""
+    X = hadamard(128).astype(F16)
+    rng = np.random.default_rng(2)
+    W = (rng.standard_normal((3, 128)) * 0.02).astype(F16)
+    res = O.search_layer(X, W, O.act_stats(X))
+    assert np.all(res.losses == res.losses[0]) and res.best == 0
+
+
+def test_argmin_rules():
+    assert O.argmin_first([3.0, 1.0, 1.0, 2.0]) == 1
+    assert O.argmin_first([np.nan, 2.0, np.inf, 2.0]) == 1
+    assert O.argmin_first([np.inf, np.nan, 5.0]) == 2
+    with pytest.raises(O.NonFiniteLosses):
+        O.argmin_first([np.nan, np.inf, np.nan])
+
+
+# --------------------------------------------------------------- invariances
+def test_weight_power_of_two_scaling():
+    X, W = _tiny_case(8, n=16, k=256, out=8)
+    sal = O.act_stats(X)
+    a = O.search_layer(X, W, sal)
+    W4 = (W.astype(F32) * 4).astype(F16)
+    b = O.search_layer(X, W4, sal)
+    assert np.allclose(b.losses, a.losses * 16, rtol=1e-12, atol=0)
+    pa, pb = O.pack(W, a.s_best), O.pack(W4, a.s_best)
+    assert np.array_equal(pa.q, pb.q) and np.array_equal(pa.zero16, pb.zero16)
+    assert np.array_equal(pb.step16.astype(F32), pa.step16.astype(F32) * 4)
+
+
+def test_activation_power_of_two_scaling():
+    X, W = _tiny_case(9, n=16, k=256, out=8)
+    a = O.search_layer(X, W, O.act_stats(X))
+    X2 = (X.astype(F32) * 2).astype(F16)
+    b = O.search_layer(X2, W, O.act_stats(X2))
+    # s changes by 2^alpha per grid point (a common factor per group), so only
+    # codes within rounding of a tie can move
+    assert np.allclose(b.losses, a.losses * 4, rtol=2e-3)
+
+
+def test_permutations():
+    X, W = _tiny_case(10, n=16, k=256, out=8)
+    sal = O.act_stats(X)
+    a = O.search_layer(X, W, sal)
+    # output rows
+    perm = np.random.default_rng(0).permutation(W.shape[0])
+    b = O.search_layer(X, W[perm], sal)
+    assert np.allclose(b.losses, a.losses, rtol=1e-12, atol=0)
+    pa, pb = O.pack(W, a.s_best), O.pack(W[perm], a.s_best)
+    assert np.array_equal(pa.qweight[perm], pb.qweight)
+    # tokens: saliency is an exact sum, hence bit-identical
+    tp = np.random.default_rng(1).permutation(X.shape[0])
+    assert np.array_equal(O.act_stats(X[tp]).view(np.uint32), sal.view(np.uint32))
+    c = O.search_layer(X[tp], W, sal)
+    assert np.allclose(c.losses, a.losses, rtol=1e-12, atol=0)
+    # whole groups of 128 columns
+    cols = np.concatenate([np.arange(128, 256), np.arange(0, 128)])
+    d = O.search_layer(X[:, cols], W[:, cols], sal[cols])
+    assert np.allclose(d.losses, a.losses, rtol=1e-12, atol=0)
+    pd = O.pack(W[:, cols], a.s_best[cols])
+    assert np.array_equal(pd.q, pa.q[:, cols])
+
+
+# ------------------------------------------------------------- error bounds
+def test_rounding_error_bound_and_zero_range():
+    """Max rounding error is half a step (dev.to 'Why does naive 4-bit
+    quantization...' and 'Salient Weight Preservation'); the zero point lies
+    in [0, 15] whenever the group straddles 0."""
+    _, X, W = synth.make_layer(1)
+    sal = O.act_stats(X)
+    s, _ = O.scale_table(sal)
+    for i in (0, 10, 19):
+        ws = O.scaled_weights(W, s[i])
+        gq = O.quantize(ws)
+        step = np.repeat(gq.step, 128, axis=1).astype(F64)
+        zero = np.repeat(gq.zero, 128, axis=1).astype(F64)
+        err = np.abs((gq.q.astype(F64) - zero) * step - ws.astype(F64))
+        x = ws.astype(F64) / step + zero
+        clamped = (x < -0.5) | (x > 15.5)
+        assert np.all(err[~clamped] <= step[~clamped] * (0.5 + 2.0 ** -18))
+        assert np.all(err <= step * (1 + 2.0 ** -18))
+        g = ws.reshape(ws.shape[0], -1, 128)
+        straddle = (g.min(axis=2) <= 0) & (g.max(axis=2) >= 0)
+        assert np.all((gq.zero[straddle] >= 0) & (gq.zero[straddle] <= 15))
+        # the group minimum always lands on code 0
+        amin = g.argmin(axis=2)
+        qg = gq.q.reshape(g.shape)
+        assert np.all(np.take_along_axis(qg, amin[:, :, None], 2) == 0)
+
+
+def test_pack_layout_and_roundtrip():
+    q = np.array([[1, 2, 3, 4, 5, 6, 7, 8, 15, 15, 15, 15, 15, 15, 15, 15]], dtype=np.uint8)
+    w = O.pack_codes(q)
+    assert w.dtype == np.int32 and w.shape == (1, 2)
+    assert w.view(np.uint32)[0, 0] == 0x87654321
+    assert w[0, 1] == -1
+    rng = np.random.default_rng(4)
+    qq = rng.integers(0, 16, (5, 256)).astype(np.uint8)
+    assert np.array_equal(O.unpack_codes(O.pack_codes(qq)), qq)
+
+
+def test_literal_division_changes_loss_negligibly():
+    """Folding s back by multiplying with fp32(1/s) instead of dividing by s
+    moves the dequantized weight by at most one fp16 rounding step."""
+    _, X, W = synth.make_layer(1)
+    sal = O.act_stats(X)
+    s, inv_s = O.scale_table(sal)
+    for i in (5, 15):
+        gq = O.quantize(O.scaled_weights(W, s[i]))
+        a = O.output_mse(X, W, O.dequantize(gq, inv_s[i]))
+        b = O.output_mse(X, W, O.dequantize(gq, inv_s[i], literal_div=s[i]))
+        assert abs(a - b) <= 1e-5 * a
+
+
+# ------------------------------------------- planted mistakes must be caught
+@pytest.mark.parametrize("mutation", ["floor_round", "symmetric_step", "grid_to_one",
+                                      "no_zero_canon"])
+def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
+    """Each plausible slip in the oracle trips at least one pin above."""
+    if mutation == "floor_round":
+        monkeypatch.setattr(O.np, "rint", np.floor)
+        with pytest.raises(AssertionError):
+            test_quantizer_matches_exact_rational_emulation(0)
+    elif mutation == "symmetric_step":
+        orig = O.quantize
+
+        def sym(ws, group=128, w_bit=4):
+            gq = orig(ws, group, w_bit)
+            g = ws.reshape(ws.shape[0], -1, group)
+            gq.step = (np.abs(g).max(axis=2) / F32(8)).astype(F32)
+            return gq
+        monkeypatch.setattr(O, "quantize", sym)
+        with pytest.raises(AssertionError):
+            test_step_equation_worked_example()
+    elif mutation == "grid_to_one":
+        monkeypatch.setattr(O, "alphas", lambda n=20: np.arange(n, dtype=F64) / (n - 1))
+        with pytest.raises(AssertionError):
+            test_single_outlier_loss_closed_form_and_monotone()
+    elif mutation == "no_zero_canon":
+        orig = O.quantize
+
+        def negz(ws, group=128, w_bit=4):
+            gq = orig(ws, group, w_bit)
+            gq.zero = np.where(gq.zero == 0, F32(-0.0), gq.zero)
+            return gq
+        monkeypatch.setattr(O, "quantize", negz)
+        with pytest.raises(AssertionError):
+            test_zero_range_group()
