@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the AWQ per-layer search path on one MI355X.
+
+A step is one pass of the whole path over every searched layer of the
+workload: saliency (awq_act_stats), the alpha-grid search (awq_search_layer:
+prepare, fused grid kernel, select) and packing at the chosen alpha
+(awq_pack).  Inputs are seeded synthetic tensors (synth/), resident in HBM
+before timing starts.  The line printed on stdout:
+
+  value        search flops of the step (20 grid points x 2 N in out, summed
+               over layers) / step time, TFLOP/s
+  roofline     the dominant kernel (the fused grid kernel): algorithmic flops
+               per launch / its mean launch time from HIP events recorded on
+               the launch stream, against the fp16 dense MFMA peak
+  kernels      per-kernel times, TFLOP/s and GB/s (stats and pack against HBM)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+
+`python bench.py --gpus N` with N > 1 exits: the path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 fp16 flop/clk (dense)
+HBM_PEAK_GBS = 8000.0
+METRIC = "AWQ α-grid search TFLOP/s + MFMA util; quant/pack HBM GB/s (1 GPU)"
+DEFAULT_CONFIG = 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def search_flops(spec, n_grid=20):
+    return 2.0 * n_grid * spec.n_tokens * spec.in_features * spec.out_features
+
+
+def stats_bytes(spec):
+    return 2.0 * spec.n_tokens * spec.in_features + 4.0 * spec.in_features
+
+
+def pack_bytes(spec):
+    w = spec.out_features * spec.in_features
+    return 2.0 * w + 0.5 * w + 4.0 * w / 128 + 4.0 * spec.in_features
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("search.hip", "awq_device.h"):
+        h.update(open(os.path.join(ROOT, "post_bit_weight_awq_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per launch of the grid kernel from the committed PMC summary,
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", "search_grid_pmc_traffic.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        m = re.match(r"\s*traffic:\s*workload=(\S+)\s+source=(\S+)\s+bytes_per_launch=(\S+)", line)
+        if m and m.group(1) == workload and m.group(2) == source_digest():
+            return float(m.group(3))
+    return None
+
+
+def cpu_baseline(cfg_key, target_s):
+    """The oracle, as it stands, on the first layer: stats on all tokens, the
+    full 20-point search and pack on a leading cut of output rows sized for
+    about target_s seconds.  Reported in the metric's unit (TFLOP/s of search
+    flops over stats + search + pack time)."""
+    import numpy as np
+    import synth
+    from oracle import awq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    spec, X, W = synth.make_layer(cfg_key, 0)
+    t0 = time.perf_counter()
+    sal = O.act_stats(X)
+    t_stats = time.perf_counter() - t0
+    # size the row cut from a probe of 1 grid point on 64 rows
+    rows = min(64, spec.out_features)
+    s, inv_s = O.scale_table(sal)
+    t0 = time.perf_counter()
+    O.tile_sq_error(X, W, s[5], inv_s[5], slice(0, spec.n_tokens), slice(0, rows))
+    per_row_alpha = (time.perf_counter() - t0) / rows
+    rows = int(max(8, min(spec.out_features, target_s / (20 * per_row_alpha + 1e-12))))
+    Wc = np.ascontiguousarray(W[:rows])
+    t0 = time.perf_counter()
+    res = O.search_layer(X, Wc, sal)
+    t_search = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.pack(Wc, res.s_best)
+    t_pack = time.perf_counter() - t0
+    flops = 2.0 * 20 * spec.n_tokens * spec.in_features * rows
+    return {
+        "value": flops / (t_stats + t_search + t_pack) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"layer {spec.name} of config {cfg_key}: stats over all {spec.n_tokens}x"
+                   f"{spec.in_features}, 20-point search and pack on the first {rows} of "
+                   f"{spec.out_features} output rows"),
+        "seconds": {"stats": t_stats, "search": t_search, "pack": t_pack},
+    }
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of a known size (PMC byte-counter scale)."""
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU; multi-GPU runs are not part of it "
+              "(each GPU would search its own share of output rows and all-reduce 20 "
+              "partial sums)", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
+
+    import numpy as np
+    import torch
+    import synth
+    import post_bit_weight_awq_amd as awq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    awq.load()
+    cfgspec = synth.CONFIGS[args.config]
+    cfg = awq.default_config()
+    layers = []
+    for li, spec in enumerate(cfgspec.layers):
+        _, X, W = synth.make_layer(args.config, li)
+        Xd = torch.from_numpy(X).cuda()
+        Wd = torch.from_numpy(W).cuda()
+        del X, W
+        n, k, o = spec.n_tokens, spec.in_features, spec.out_features
+        L = dict(spec=spec, X=Xd, W=Wd,
+                 sal=torch.empty(k, dtype=torch.float32, device="cuda"),
+                 sws=torch.empty(awq.awq_act_stats_workspace_size(n, k), dtype=torch.uint8,
+                                 device="cuda"),
+                 ws=torch.empty(awq.awq_search_workspace_size(n, k, o, cfg), dtype=torch.uint8,
+                                device="cuda"),
+                 losses=torch.empty(cfg.n_grid, dtype=torch.float64, device="cuda"),
+                 best=torch.empty(1, dtype=torch.int32, device="cuda"),
+                 s_best=torch.empty(k, dtype=torch.float32, device="cuda"),
+                 qw=torch.empty((o, k // 8), dtype=torch.int32, device="cuda"),
+                 st=torch.empty((o, k // 128), dtype=torch.float16, device="cuda"),
+                 zr=torch.empty((o, k // 128), dtype=torch.float16, device="cuda"))
+        layers.append(L)
+        log(f"layer {spec.name}: {n}x{k}->{o}")
+    torch.cuda.synchronize()
+
+    names = ("stats", "prepare", "grid", "select", "pack")
+
+    def step(events=None):
+        for li, L in enumerate(layers):
+            ev = events[li] if events is not None else None
+
+            def mark(j):
+                if ev is not None:
+                    ev[j].record()
+            mark(0)
+            awq.awq_act_stats(L["X"], out=L["sal"], workspace=L["sws"])
+            mark(1)
+            for j, stg in enumerate((awq.STAGE_PREPARE, awq.STAGE_GRID, awq.STAGE_SELECT)):
+                awq.awq_search_layer(L["X"], L["W"], L["sal"], cfg, workspace=L["ws"],
+                                     losses=L["losses"], best_idx=L["best"],
+                                     s_best=L["s_best"], stages=stg)
+                mark(2 + j)
+            awq.awq_pack(L["W"], L["s_best"], cfg, qweight=L["qw"], step=L["st"], zero=L["zr"])
+            mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # events on torch's current stream, which is the stream every call launches on
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in layers]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per = {nm: [0.0] * len(layers) for nm in names}
+    for s in range(args.steps):
+        for li in range(len(layers)):
+            e = evs[s][li]
+            for j, nm in enumerate(names):
+                per[nm][li] += e[j].elapsed_time(e[j + 1]) / args.steps
+
+    F = [search_flops(L["spec"], cfg.n_grid) for L in layers]
+    total_F = sum(F)
+    value = total_F / (ms_per_step * 1e-3) / 1e12
+    grid_ms = sum(per["grid"])
+    achieved = total_F / (grid_ms * 1e-3) / 1e12
+    kernels = {}
+    for li, L in enumerate(layers):
+        spec = L["spec"]
+        kernels[spec.name] = {
+            "shape": [spec.n_tokens, spec.in_features, spec.out_features],
+            "best_idx": int(L["best"].item()),
+            "ms": {nm: round(per[nm][li], 5) for nm in names},
+            "grid_tflops": round(F[li] / (per["grid"][li] * 1e-3) / 1e12, 2),
+            "search_tflops": round(F[li] / ((per["prepare"][li] + per["grid"][li] +
+                                             per["select"][li]) * 1e-3) / 1e12, 2),
+            "stats_gbs": round(stats_bytes(spec) / (per["stats"][li] * 1e-3) / 1e9, 1),
+            "pack_gbs": round(pack_bytes(spec) / (per["pack"][li] * 1e-3) / 1e9, 1),
+        }
+    traffic = traffic_from_profiles(cfgspec.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded generators, outlier-channel activations, N(0,0.02) weights)",
+        "config": {"workload": cfgspec.workload, "layers": [
+            {"name": L["spec"].name, "n_tokens": L["spec"].n_tokens,
+             "in_features": L["spec"].in_features, "out_features": L["spec"].out_features}
+            for L in layers], "group_size": 128, "w_bit": 4, "n_grid": cfg.n_grid},
+        "roofline": {"bound": "mfma", "kernel": "k_tile (fused grid search)",
+                     "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "grid_ms_per_launch": round(grid_ms / len(layers), 5)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * awq_mi355x.h -- C ABI of the MI355X (gfx950) AWQ per-layer search library.
+ *
+ * The library computes, for one linear layer at a time, the data-parallel core
+ * of activation-aware weight quantization (AWQ):
+ *
+ *   1. activation saliency     sal_k = mean_t |X[t,k]|
+ *   2. per-channel scales      s_i,k = max(sal_k, floor) ^ alpha_i, alpha_i = i / n_grid
+ *   3. group quantization      of W diag(s_i): asymmetric INT4, groups of 128 along
+ *                              in_features, step = (max - min) / 15,
+ *                              zero = rint(-min / step), q = clamp(rint(w/step) + zero, 0, 15)
+ *   4. dequantize and unscale  Wq_i = fp16(((q - zero) * step) * (1 / s_i))
+ *   5. loss and choice         L_i = mean over tokens and outputs of (X Wq_i^T - X W^T)^2,
+ *                              i* = first index of the minimum finite L_i; the codes of
+ *                              W diag(s_i*) are then packed eight nibbles per int32 with
+ *                              fp16 step and zero point per group.
+ *
+ * Sources, by page and section:
+ *   - dev.to "AWQ: How Activation-Aware Quantization Saves 4-bit LLMs":
+ *     channel_importance listing (step 1), search_scale listing (steps 2-5),
+ *     "What do you actually deploy" (zero point, group 128, 4 bit).
+ *   - mbrenndoerfer.com "AWQ > Salient Weight Preservation": step-size equation
+ *     (step 3) and the scaling identity (why step 4 divides by s).
+ *   - mbrenndoerfer.com "AWQ > Summary": saliency is the average absolute
+ *     activation; one alpha per layer from a grid search.
+ *   - esaholic.com "What is AWQ Quantization?", pipeline step "INT4 Weight
+ *     Packing & Export": codes are packed into INT32 containers.
+ *
+ * Conventions for every call:
+ *   - All tensors are dense, row-major, and live in device memory of the GPU
+ *     that is current on the calling thread.  The caller owns every buffer;
+ *     the library never allocates or frees device memory and keeps no device
+ *     state between calls.  Scratch memory is a caller-provided workspace whose
+ *     size the matching *_workspace_size call returns.
+ *   - Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work and return; results are valid once the stream has reached them.
+ *     Calls on different streams with disjoint buffers may run concurrently.
+ *   - Every argument is validated on the host before anything is enqueued; a
+ *     failed check enqueues nothing and returns a negative awq_status.  A launch
+ *     failure returns AWQ_ERR_HIP.  awq_last_error() then describes the failure
+ *     (a thread-local string, valid until the thread's next call).
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment       */
+  AWQ_ERR_UNSUPPORTED = -2, /* configuration outside what is implemented  */
+  AWQ_ERR_WORKSPACE = -3,   /* workspace smaller than the queried size    */
+  AWQ_ERR_HIP = -4          /* the HIP runtime reported an error          */
+} awq_status;
+
+/* Quantization settings (the quant_config of the dev.to page's "What do you
+ * actually deploy" section, plus the search_scale listing's grid size and
+ * saliency floor).  Only w_bit = 4, group_size = 128 and zero_point = 1 are
+ * implemented; n_grid may be 1..64; sal_floor must be finite and > 0. */
+typedef struct awq_config {
+  int32_t w_bit;      /* bits per code: 4                                  */
+  int32_t group_size; /* weights per step/zero along in_features: 128      */
+  int32_t n_grid;     /* grid points alpha_i = i / n_grid: default 20      */
+  float sal_floor;    /* saliency clamp before the power: default 1e-4f    */
+  int32_t zero_point; /* asymmetric quantization with a zero point: 1      */
+} awq_config;
+
+/* Fills *cfg with the defaults {4, 128, 20, 1e-4f, 1}. */
+void awq_default_config(awq_config* cfg);
+
+/* Thread-local description of the last failed call on this thread ("" if none). */
+const char* awq_last_error(void);
+
+/* Library version string. */
+const char* awq_version(void);
+
+/* ------------------------------------------------------------------------
+ * Step 1: activation statistics.
+ * sal_out[k] = fp32( (sum_t |X[t,k]|) / n_tokens ), the sum exact (fp16
+ * magnitudes are summed as integers in units of 2^-24), the quotient taken in
+ * binary64 and rounded to binary32.
+ *   X:        [n_tokens, in_features] fp16, read only
+ *   sal_out:  [in_features] fp32, written
+ *   n_tokens >= 1, in_features >= 8 and a multiple of 8.
+ * Source: dev.to page, channel_importance listing; Summary page,
+ * "Salient weight identification".
+ * ---------------------------------------------------------------------- */
+size_t awq_act_stats_workspace_size(int64_t n_tokens, int64_t in_features);
+int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Steps 2-5: the alpha-grid search of one layer, all grid points in one pass.
+ *   X:            [n_tokens, in_features] fp16
+ *   W:            [out_features, in_features] fp16 (fused layers: rows concatenated)
+ *   sal:          [in_features] fp32 (from awq_act_stats or any source)
+ *   losses_out:   [n_grid] float64: L_i, the mean squared output error
+ *   best_idx_out: [1] int32: i*, or -1 when no L_i is finite
+ *   s_best_out:   [in_features] fp32: s_i* (all NaN when i* = -1)
+ *   in_features must be a multiple of group_size; n_tokens, out_features >= 1.
+ * The workspace (size from awq_search_workspace_size) holds the scale table,
+ * the per-group quantizer parameters, the reference output X W^T in fp32 and
+ * the per-tile partial sums; awq_search_plan describes where.
+ * Source: dev.to page, search_scale listing; Salient Weight Preservation page,
+ * step-size equation.
+ * ---------------------------------------------------------------------- */
+typedef struct awq_search_plan {
+  int64_t tile_tokens;     /* tokens per output tile                               */
+  int64_t tile_out;        /* output features per output tile                      */
+  int64_t n_token_tiles;   /* ceil(n_tokens / tile_tokens)                         */
+  int64_t n_out_tiles;     /* ceil(out_features / tile_out)                        */
+  size_t partials_offset;  /* double [n_grid][n_token_tiles][n_out_tiles]: sum of
+                              squared differences over each tile (not averaged)   */
+  size_t yref_offset;      /* float [n_tokens][out_features]: X W^T                */
+  size_t scales_offset;    /* float [n_grid][in_features]: s_i                     */
+  size_t workspace_bytes;  /* total workspace size                                 */
+} awq_search_plan;
+
+int awq_search_plan_query(int64_t n_tokens, int64_t in_features, int64_t out_features,
+                          const awq_config* cfg, awq_search_plan* plan);
+size_t awq_search_workspace_size(int64_t n_tokens, int64_t in_features, int64_t out_features,
+                                 const awq_config* cfg);
+int awq_search_layer(const void* X, const void* W, const float* sal, int64_t n_tokens,
+                     int64_t in_features, int64_t out_features, const awq_config* cfg,
+                     double* losses_out, int32_t* best_idx_out, float* s_best_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same search split into its three stages, for callers that time or
+ * overlap them: stage_mask is an OR of the AWQ_STAGE_* bits, and
+ * awq_search_layer(...) equals awq_search_layer_stages(AWQ_STAGE_ALL, ...).
+ * A stage reads what the earlier stages left in the workspace, so the stages of
+ * one search must run in order, on one workspace, with the same arguments.
+ *   AWQ_STAGE_PREPARE: scale table, per-group quantizer parameters of every
+ *                      grid point, and the reference output X W^T
+ *   AWQ_STAGE_GRID:    the fused quantize-dequantize + MFMA contraction +
+ *                      squared-error kernel over all grid points
+ *   AWQ_STAGE_SELECT:  losses, argmin and s_best */
+#define AWQ_STAGE_PREPARE 1
+#define AWQ_STAGE_GRID 2
+#define AWQ_STAGE_SELECT 4
+#define AWQ_STAGE_ALL 7
+int awq_search_layer_stages(int stage_mask, const void* X, const void* W, const float* sal,
+                            int64_t n_tokens, int64_t in_features, int64_t out_features,
+                            const awq_config* cfg, double* losses_out, int32_t* best_idx_out,
+                            float* s_best_out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * Packing: quantize W diag(s) (exact IEEE division for every code) and pack.
+ *   W:            [out_features, in_features] fp16
+ *   s:            [in_features] fp32, any positive scales (normally s_best_out)
+ *   qweight_out:  [out_features, in_features / 8] int32; nibble j (bits 4j..4j+3)
+ *                 of word w holds the code of column 8w + j
+ *   step_out:     [out_features, in_features / group_size] fp16
+ *   zero_out:     [out_features, in_features / group_size] fp16 (integer values)
+ * A group whose values are all equal takes step = 1.
+ * Source: esaholic.com page, "INT4 Weight Packing & Export"; dev.to page,
+ * quant_config; modelrefs.com page, memory example (one 16-bit scale per 128).
+ * ---------------------------------------------------------------------- */
+int awq_pack(const void* W, const float* s, int64_t in_features, int64_t out_features,
+             const awq_config* cfg, int32_t* qweight_out, void* step_out, void* zero_out,
+             void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_H */

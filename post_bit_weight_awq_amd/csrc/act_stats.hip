@@ -1,0 +1,125 @@
+// Step 1 of the AWQ search: per-input-channel activation saliency
+// sal_k = mean_t |X[t,k]|   (dev.to "AWQ: How Activation-Aware Quantization
+// Saves 4-bit LLMs", channel_importance listing; "AWQ > Summary", salient
+// weight identification: average absolute activation over the calibration set).
+//
+// HBM-bound column reduction.  Each lane owns 8 consecutive columns and reads
+// them with one 16-byte load per token row, so a wavefront reads 1 KiB of a row
+// contiguously.  The block's four wavefronts take interleaved rows of one row
+// chunk.  |x| of an fp16 value is an integer multiple of 2^-24 below 2^16, so
+// the per-lane binary64 sums are exact (at most 8192 rows per chunk), and the
+// block total is added into a 64-bit integer accumulator in units of 2^-24:
+// the result is exact and independent of the order of the additions.
+#include "awq_device.h"
+#include "awq_internal.h"
+
+namespace awq {
+
+constexpr int kStatsThreads = 256;
+constexpr int kStatsCols = kWave * 8;  // columns per block
+
+__global__ void __launch_bounds__(256) k_fill_u64(unsigned long long* p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+__global__ void __launch_bounds__(kStatsThreads)
+k_act_stats(const uint4* __restrict__ X, int64_t n_tokens, int64_t in_features,
+            int64_t rows_per_chunk, unsigned long long* __restrict__ acc) {
+  __shared__ double red[kStatsThreads / kWave][kStatsCols];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int64_t col = (int64_t)blockIdx.x * kStatsCols + lane * 8;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+  const int64_t r1 = min(r0 + rows_per_chunk, n_tokens);
+  const int64_t row_vecs = in_features / 8;  // uint4 per row
+  double s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = 0.0;
+  if (col < in_features) {
+    const uint4* p = X + r0 * row_vecs + col / 8;
+    int64_t r = r0 + wave;
+    // four rows in flight per lane
+    for (; r + 12 < r1; r += 16) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = p[(r - r0 + 4 * u) * row_vecs];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[2 * j] += (double)fabsf(f16_lo(w[j]));
+          s[2 * j + 1] += (double)fabsf(f16_hi(w[j]));
+        }
+      }
+    }
+    for (; r < r1; r += 4) {
+      const uint4 v = p[(r - r0) * row_vecs];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[2 * j] += (double)fabsf(f16_lo(w[j]));
+        s[2 * j + 1] += (double)fabsf(f16_hi(w[j]));
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[wave][lane * 8 + j] = s[j];
+  __syncthreads();
+  // 512 column totals, two per thread; the four wave partials are exact, so
+  // their sum is exact as well.
+  for (int c = threadIdx.x; c < kStatsCols; c += kStatsThreads) {
+    const int64_t gc = (int64_t)blockIdx.x * kStatsCols + c;
+    if (gc < in_features) {
+      double t = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+      unsigned long long u = (unsigned long long)(t * 16777216.0);  // exact: t is a multiple of 2^-24
+      if (u) atomicAdd(acc + gc, u);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+k_stats_finalize(const unsigned long long* __restrict__ acc, int64_t in_features,
+                 int64_t n_tokens, float* __restrict__ sal) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < in_features) {
+    // binary64 value of the exact sum (rounded only beyond 2^53 units), then
+    // the binary64 quotient, then binary32.
+    double total = (double)acc[k] * 0x1p-24;
+    sal[k] = (float)(total / (double)n_tokens);
+  }
+}
+
+StatsPlan stats_plan(int64_t n_tokens, int64_t in_features) {
+  StatsPlan p;
+  p.col_blocks = (in_features + kStatsCols - 1) / kStatsCols;
+  // enough blocks to cover the chip several times over, chunks of >= 16 rows
+  int64_t want = (2048 + p.col_blocks - 1) / p.col_blocks;
+  int64_t max_chunks = (n_tokens + 15) / 16;
+  p.row_chunks = want < max_chunks ? want : max_chunks;
+  if (p.row_chunks < 1) p.row_chunks = 1;
+  p.rows_per_chunk = (n_tokens + p.row_chunks - 1) / p.row_chunks;
+  if (p.rows_per_chunk > 8192) {  // keep the per-lane binary64 sums exact
+    p.rows_per_chunk = 8192;
+  }
+  p.row_chunks = (n_tokens + p.rows_per_chunk - 1) / p.rows_per_chunk;
+  p.workspace_bytes = (size_t)in_features * sizeof(unsigned long long);
+  return p;
+}
+
+hipError_t launch_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal,
+                            void* workspace, hipStream_t stream) {
+  const StatsPlan p = stats_plan(n_tokens, in_features);
+  unsigned long long* acc = (unsigned long long*)workspace;
+  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)((in_features + 255) / 256)), dim3(256), 0, stream,
+                     acc, in_features);
+  hipLaunchKernelGGL(k_act_stats, dim3((unsigned)p.col_blocks, (unsigned)p.row_chunks),
+                     dim3(kStatsThreads), 0, stream, (const uint4*)X, n_tokens, in_features,
+                     p.rows_per_chunk, acc);
+  hipLaunchKernelGGL(k_stats_finalize, dim3((unsigned)((in_features + 255) / 256)), dim3(256), 0,
+                     stream, acc, in_features, n_tokens, sal);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -1,0 +1,58 @@
+// Device-side helpers shared by the gfx950 kernels of the AWQ search library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kGroup = 128;
+
+// Bit pattern of -0.0f.  Used as the addend of the mixed-precision FMAs below:
+// a*b + (-0) equals the rounded product a*b for every a, b (signed zeros
+// included), so those FMAs are exact products with a single rounding.
+__device__ __forceinline__ float neg_zero() { return __uint_as_float(0x80000000u); }
+
+// fp32(h * s) where h is the low (HI=false) or high (HI=true) fp16 half of `w2`.
+// The fp16 operand is widened exactly, so this equals fp32(fp32(h) * s).
+template <bool HI>
+__device__ __forceinline__ float mul_f16_f32(uint32_t w2, float s, float nz) {
+  float r;
+  if (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(w2), "v"(s), "v"(nz));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(w2), "v"(s), "v"(nz));
+  return r;
+}
+
+// Two fp16 values packed in one register: lo = fp16(a0 * b0), hi = fp16(a1 * b1),
+// each product of two fp32 values rounded ONCE (to nearest even) to fp16.
+__device__ __forceinline__ uint32_t mul_f32_to_f16x2(float a0, float b0, float a1, float b1,
+                                                     float nz) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]"
+      : "=v"(r) : "v"(a0), "v"(b0), "v"(nz));
+  asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]"
+      : "+v"(r) : "v"(a1), "v"(b1), "v"(nz));
+  return r;
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+__device__ __forceinline__ float med3(float x, float lo, float hi) {
+  return __builtin_amdgcn_fmed3f(x, lo, hi);
+}
+
+}  // namespace awq

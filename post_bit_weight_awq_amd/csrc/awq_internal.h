@@ -1,0 +1,36 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace awq {
+
+struct StatsPlan {
+  int64_t col_blocks;
+  int64_t row_chunks;
+  int64_t rows_per_chunk;
+  size_t workspace_bytes;
+};
+StatsPlan stats_plan(int64_t n_tokens, int64_t in_features);
+hipError_t launch_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal,
+                            void* workspace, hipStream_t stream);
+
+struct SearchPlan {
+  int64_t tile_m, tile_n;        // tokens x outputs per tile
+  int64_t n_t_tiles, n_o_tiles;  // tile counts
+  int kernel;                    // which tile kernel variant
+  size_t off_partials, off_yref, off_s, off_inv_s, off_params;
+  size_t bytes;
+};
+SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid);
+hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t n_tokens,
+                         int64_t in_features, int64_t out_features, int n_grid, float sal_floor,
+                         double* losses, int32_t* best_idx, float* s_best, void* workspace,
+                         const SearchPlan& plan, int stage_mask, hipStream_t stream);
+
+hipError_t launch_pack(const void* W, const float* s, int64_t in_features, int64_t out_features,
+                       int32_t* qweight, void* step16, void* zero16, hipStream_t stream);
+
+}  // namespace awq

@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/awq_mi355x.h declares, and rejects bad arguments on the host before
+anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from post_bit_weight_awq_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq_mi355x.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libawq_mi355x.so is not built (run post_bit_weight_awq_amd/build.py)")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_default_config_and_version(lib):
+    cfg = _lib.AwqConfig()
+    lib.awq_default_config(ctypes.byref(cfg))
+    assert (cfg.w_bit, cfg.group_size, cfg.n_grid, cfg.zero_point) == (4, 128, 20, 1)
+    assert cfg.sal_floor == pytest.approx(1e-4, rel=1e-6)
+    assert b"gfx950" in lib.awq_version()
+
+
+def _cfg(lib, **kw):
+    cfg = _lib.AwqConfig()
+    lib.awq_default_config(ctypes.byref(cfg))
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+FAKE = ctypes.c_void_p(0x1000)      # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x1004)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w_bit=3), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(group_size=64), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(zero_point=0), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(n_grid=0), _lib.AWQ_ERR_INVALID_ARG),
+    (dict(n_grid=65), _lib.AWQ_ERR_INVALID_ARG),
+    (dict(sal_floor=0.0), _lib.AWQ_ERR_INVALID_ARG),
+    (dict(sal_floor=float("nan")), _lib.AWQ_ERR_INVALID_ARG),
+])
+def test_search_rejects_bad_config(lib, kw, code):
+    cfg = _cfg(lib, **kw)
+    rc = lib.awq_search_layer(FAKE, FAKE, FAKE, 128, 512, 512, ctypes.byref(cfg), FAKE, FAKE,
+                              FAKE, FAKE, 1 << 40, None)
+    assert rc == code
+    assert lib.awq_last_error()
+    rc = lib.awq_pack(FAKE, FAKE, 512, 512, ctypes.byref(cfg), FAKE, FAKE, FAKE, None)
+    assert rc == code
+
+
+@pytest.mark.parametrize("n,k,o", [(0, 512, 512), (128, 500, 512), (128, 512, 0),
+                                   (128, 0, 512), ((1 << 24) + 1, 512, 512),
+                                   (128, 1 << 21, 8)])
+def test_search_rejects_bad_shapes(lib, n, k, o):
+    cfg = _cfg(lib)
+    rc = lib.awq_search_layer(FAKE, FAKE, FAKE, n, k, o, ctypes.byref(cfg), FAKE, FAKE, FAKE,
+                              FAKE, 1 << 40, None)
+    assert rc == _lib.AWQ_ERR_INVALID_ARG
+    assert lib.awq_search_workspace_size(n, k, o, ctypes.byref(cfg)) == 0
+
+
+def test_search_rejects_null_and_misaligned(lib):
+    cfg = _cfg(lib)
+    args = [FAKE, FAKE, FAKE, 128, 512, 512, ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, 1 << 40,
+            None]
+    for pos in (0, 1, 2, 7, 8, 9, 10):
+        a = list(args)
+        a[pos] = None
+        assert lib.awq_search_layer(*a) == _lib.AWQ_ERR_INVALID_ARG, pos
+    for pos in (0, 1, 2, 7, 9, 10):
+        a = list(args)
+        a[pos] = MISALIGNED
+        assert lib.awq_search_layer(*a) == _lib.AWQ_ERR_INVALID_ARG, pos
+        assert b"aligned" in lib.awq_last_error()
+
+
+def test_search_workspace_too_small(lib):
+    cfg = _cfg(lib)
+    need = lib.awq_search_workspace_size(128, 512, 512, ctypes.byref(cfg))
+    assert need > 0
+    rc = lib.awq_search_layer(FAKE, FAKE, FAKE, 128, 512, 512, ctypes.byref(cfg), FAKE, FAKE,
+                              FAKE, FAKE, need - 1, None)
+    assert rc == _lib.AWQ_ERR_WORKSPACE
+
+
+def test_search_plan_layout(lib):
+    cfg = _cfg(lib)
+    plan = _lib.AwqSearchPlan()
+    assert lib.awq_search_plan_query(1000, 4096, 1000, ctypes.byref(cfg), ctypes.byref(plan)) == 0
+    assert plan.n_token_tiles == -(-1000 // plan.tile_tokens)
+    assert plan.n_out_tiles == -(-1000 // plan.tile_out)
+    regions = sorted([
+        (plan.partials_offset, 8 * 20 * plan.n_token_tiles * plan.n_out_tiles),
+        (plan.yref_offset, 4 * 1000 * 1000),
+        (plan.scales_offset, 4 * 20 * 4096)])
+    for (a, la), (b, _) in zip(regions, regions[1:]):
+        assert a + la <= b
+    assert regions[-1][0] + regions[-1][1] <= plan.workspace_bytes
+    for off in (plan.partials_offset, plan.yref_offset, plan.scales_offset):
+        assert off % 256 == 0
+
+
+def test_stats_validation(lib):
+    assert lib.awq_act_stats_workspace_size(0, 512) == 0
+    assert lib.awq_act_stats_workspace_size(10, 12) == 0
+    need = lib.awq_act_stats_workspace_size(10, 512)
+    assert need >= 8 * 512
+    assert lib.awq_act_stats(None, 10, 512, FAKE, FAKE, need, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert lib.awq_act_stats(FAKE, 10, 512, FAKE, FAKE, need - 8, None) == _lib.AWQ_ERR_WORKSPACE
+    assert lib.awq_act_stats(FAKE, 10, 512, MISALIGNED, FAKE, need, None) == _lib.AWQ_ERR_INVALID_ARG
+
+
+def test_pack_validation(lib):
+    cfg = _cfg(lib)
+    assert lib.awq_pack(FAKE, FAKE, 100, 4, ctypes.byref(cfg), FAKE, FAKE, FAKE, None) \
+        == _lib.AWQ_ERR_INVALID_ARG
+    assert lib.awq_pack(FAKE, FAKE, 128, 4, ctypes.byref(cfg), FAKE, None, FAKE, None) \
+        == _lib.AWQ_ERR_INVALID_ARG
+    assert lib.awq_pack(FAKE, FAKE, 128, 4, ctypes.byref(cfg), FAKE, ctypes.c_void_p(0x1001),
+                        FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert lib.awq_pack(FAKE, FAKE, 128, 4, None, FAKE, FAKE, FAKE, None) \
+        == _lib.AWQ_ERR_INVALID_ARG
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import post_bit_weight_awq_amd as awq
+    X = torch.zeros(4, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        awq.awq_act_stats(X, out=torch.empty(128), workspace=torch.empty(4096, dtype=torch.uint8))

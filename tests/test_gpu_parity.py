@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (element by element, same seeded inputs on both sides):
+  * saliency: bit-exact (both sides sum exactly);
+  * packed codes, steps, zero points: bit-exact (both divide exactly);
+  * per-grid-point losses: within 1e-3 relative (observed far tighter);
+  * chosen index: identical unless the oracle's two best losses lie within
+    1e-3 relative of each other; s_best bit-exact against the oracle's s row;
+  * full-size layers: per-tile partial sums of sampled tiles within 1e-3
+    relative of the oracle's block sums, sampled X W^T values within fp32
+    accumulation error, and the loss/argmin consistent with those partials.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import synth
+from oracle import awq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+LOSS_RTOL = 1e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def awq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_bit_weight_awq_amd as m
+    m.load()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def run_layer(awq, X, W, n_grid=20):
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    res = awq.awq_search_layer(Xd, Wd, sal, awq.default_config(n_grid=n_grid))
+    torch.cuda.synchronize()
+    return Xd, Wd, sal, res
+
+
+def check_best(gpu_best, ref_losses):
+    order = np.argsort(ref_losses, kind="stable")
+    best = O.argmin_first(ref_losses)
+    if gpu_best == best:
+        return
+    second = ref_losses[order[1]]
+    assert abs(second - ref_losses[best]) <= LOSS_RTOL * ref_losses[best], (gpu_best, best)
+    assert gpu_best in order[:2]
+
+
+# ------------------------------------------------------------------ stats
+STATS_CASES = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (5, 0), (5, 3)]
+
+
+@pytest.mark.parametrize("cfg,layer", STATS_CASES)
+def test_stats_bitexact_configs(awq, cfg, layer):
+    _say(f"stats config {cfg} layer {layer}")
+    _, X, _ = synth.make_layer(cfg, layer, out_features=1)
+    sal = host(awq.awq_act_stats(dev(X)))
+    ref = O.act_stats(X)
+    assert np.array_equal(sal.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k", [(1, 8), (37, 520), (3, 4096), (1000, 136), (9000, 64)])
+def test_stats_edge_shapes(awq, n, k):
+    _say(f"stats edge {n}x{k}")
+    rng = np.random.default_rng(n * 7 + k)
+    X = (rng.standard_normal((n, k)) * rng.choice([1e-6, 1.0, 3e3], size=k)).astype(np.float16)
+    X[0, 0] = np.float16(65504.0)
+    if k > 1:
+        X[0, 1] = np.float16(2.0 ** -24)
+    sal = host(awq.awq_act_stats(dev(X)))
+    assert np.array_equal(sal.view(np.uint32), O.act_stats(X).view(np.uint32))
+
+
+# -------------------------------------------------------------------- pack
+PACK_CASES = [(1, 0), (2, 0), (3, 0), (4, 1), (5, 2)]
+
+
+@pytest.mark.parametrize("cfg,layer", PACK_CASES)
+def test_pack_bitexact_configs(awq, cfg, layer):
+    _say(f"pack config {cfg} layer {layer}")
+    spec, X, W = synth.make_layer(cfg, layer, n_tokens=64)
+    sal = O.act_stats(X)
+    s, _ = O.scale_table(sal)
+    s_row = s[13]
+    qw, st, zr = awq.awq_pack(dev(W), dev(s_row))
+    ref = O.pack(W, s_row)
+    qw, st, zr = host(qw), host(st), host(zr)
+    assert np.array_equal(qw, ref.qweight)
+    assert np.array_equal(st.view(np.uint16), ref.step16.view(np.uint16))
+    assert np.array_equal(zr.view(np.uint16), ref.zero16.view(np.uint16))
+
+
+def test_pack_edge_groups(awq):
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((5, 384)) * 0.02).astype(np.float16)
+    W[0, :128] = 0                              # zero range: step 1
+    W[1, 128:256] = np.float16(0.25)            # constant group
+    W[2, 256:] = np.abs(W[2, 256:]) + np.float16(0.01)   # all-positive group
+    W[3, :128] = (np.arange(128) % 16 - 5) / 16  # on the grid (exact ties of the quotient)
+    s = rng.uniform(0.25, 4.0, 384).astype(np.float32)
+    s[:128] = 1.0
+    qw, st, zr = (host(t) for t in awq.awq_pack(dev(W), dev(s)))
+    ref = O.pack(W, s)
+    assert np.array_equal(qw, ref.qweight)
+    assert np.array_equal(st.view(np.uint16), ref.step16.view(np.uint16))
+    assert np.array_equal(zr.view(np.uint16), ref.zero16.view(np.uint16))
+
+
+# ----------------------------------------------- search: oracle-sized cases
+SEARCH_SMALL = [
+    ("cfg1", dict(config=1)),
+    ("cfg2", dict(config=2)),
+    ("cfg3_cut", dict(config=3, n_tokens=200, out_features=300)),
+    ("cfg4_up_cut", dict(config=4, layer=0, n_tokens=130, out_features=260)),
+    ("cfg4_down_cut", dict(config=4, layer=1, n_tokens=96, out_features=200)),
+    ("cfg5_qkv_cut", dict(config=5, layer=0, n_tokens=160, out_features=256)),
+    ("cfg5_down_cut", dict(config=5, layer=3, n_tokens=64, out_features=136)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SEARCH_SMALL, ids=[c[0] for c in SEARCH_SMALL])
+def test_search_matches_oracle(awq, name, kw):
+    config = kw.pop("config")
+    layer = kw.pop("layer", 0)
+    _say(f"search {name}")
+    spec, X, W = synth.make_layer(config, layer, **kw)
+    Xd, Wd, sal, res = run_layer(awq, X, W)
+    sal_h = host(sal)
+    ref = O.search_layer(X, W, sal_h)
+    losses = host(res.losses)
+    rel = np.abs(losses - ref.losses) / ref.losses
+    _say(f"  max rel loss diff {rel.max():.3e}; best gpu {int(host(res.best_idx)[0])} "
+         f"oracle {ref.best}")
+    assert np.all(rel <= LOSS_RTOL)
+    best = int(host(res.best_idx)[0])
+    check_best(best, ref.losses)
+    assert np.array_equal(host(res.s_best).view(np.uint32), ref.s[best].view(np.uint32))
+    # then pack at the GPU's choice: bit-exact against the oracle at the same s
+    qw, st, zr = (host(t) for t in awq.awq_pack(Wd, res.s_best))
+    pref = O.pack(W, ref.s[best])
+    assert np.array_equal(qw, pref.qweight)
+    assert np.array_equal(st.view(np.uint16), pref.step16.view(np.uint16))
+
+
+def test_search_is_deterministic(awq):
+    _, X, W = synth.make_layer(3, n_tokens=256, out_features=512)
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    a = host(awq.awq_search_layer(Xd, Wd, sal).losses)
+    b = host(awq.awq_search_layer(Xd, Wd, sal).losses)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_search_on_side_stream(awq):
+    _, X, W = synth.make_layer(1)
+    Xd, Wd = dev(X), dev(W)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        sal = awq.awq_act_stats(Xd)
+        r = awq.awq_search_layer(Xd, Wd, sal)
+    s.synchronize()
+    ref = O.search_layer(X, W, O.act_stats(X))
+    assert np.allclose(r.losses.cpu().numpy(), ref.losses, rtol=LOSS_RTOL)
+
+
+# ------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("n,k,o,n_grid", [(1, 128, 1, 20), (5, 128, 3, 1), (33, 256, 129, 64),
+                                          (129, 384, 257, 7)])
+def test_search_edge_shapes(awq, n, k, o, n_grid):
+    _say(f"search edge {n}x{k}->{o} grid {n_grid}")
+    _, X, W = synth.make_custom(n, k, o, seed=n + k + o)
+    Xd, Wd, sal, res = run_layer(awq, X, W, n_grid=n_grid)
+    ref = O.search_layer(X, W, host(sal), n_grid=n_grid)
+    losses = host(res.losses)
+    assert losses.shape == (n_grid,)
+    assert np.all(np.abs(losses - ref.losses) <= LOSS_RTOL * ref.losses)
+    check_best(int(host(res.best_idx)[0]), ref.losses)
+
+
+def test_search_degenerate_inputs(awq):
+    # all-zero activations: saliency 0 is floored, every loss is 0, the first wins
+    X = np.zeros((16, 256), np.float16)
+    W = (np.random.default_rng(0).standard_normal((8, 256)) * 0.02).astype(np.float16)
+    _, _, sal, res = run_layer(awq, X, W)
+    assert np.all(host(res.losses) == 0) and int(host(res.best_idx)[0]) == 0
+    # Hadamard activations: |x| = 1 gives s = 1 for every alpha, equal losses, index 0
+    h = np.array([[1.0]])
+    while h.shape[0] < 128:
+        h = np.block([[h, h], [h, -h]])
+    X = h.astype(np.float16)
+    _, _, sal, res = run_layer(awq, X, W[:, :128].copy())
+    losses = host(res.losses)
+    assert np.all(losses == losses[0]) and int(host(res.best_idx)[0]) == 0
+    # a NaN weight makes every loss NaN: no choice, s_best all NaN
+    Wn = W.copy()
+    Wn[0, 0] = np.float16(np.nan)
+    _, _, sal, res = run_layer(awq, np.ones((4, 256), np.float16), Wn)
+    assert int(host(res.best_idx)[0]) == -1
+    assert np.all(np.isnan(host(res.s_best)))
+
+
+# ------------------------------------------- full-size layers, tile sampled
+FULL = [(2, 0), (3, 0), (4, 0), (4, 1), (5, 0), (5, 1), (5, 2), (5, 3)]
+
+
+@pytest.mark.parametrize("cfg,layer", FULL)
+def test_full_size_layer_sampled_tiles(awq, cfg, layer):
+    spec, X, W = synth.make_layer(cfg, layer)
+    _say(f"full-size config {cfg} layer {spec.name}: {spec.n_tokens}x{spec.in_features}"
+         f"->{spec.out_features}")
+    Xd, Wd, sal, res = run_layer(awq, X, W)
+    sal_h = host(sal)
+    assert np.array_equal(sal_h.view(np.uint32), O.act_stats(X).view(np.uint32))
+    plan = res.plan
+    ws = res.workspace
+    n_grid = 20
+    nt, no = plan.n_token_tiles, plan.n_out_tiles
+    part = host(ws[plan.partials_offset:plan.partials_offset + 8 * n_grid * nt * no]
+                .view(torch.float64)).reshape(n_grid, nt, no)
+    losses = host(res.losses)
+    count = float(spec.n_tokens) * spec.out_features
+    assert np.allclose(losses, part.reshape(n_grid, -1).sum(axis=1) / count, rtol=1e-12)
+    best = int(host(res.best_idx)[0])
+    assert best == O.argmin_first(losses)
+    s_tab, inv_s = O.scale_table(sal_h)
+    assert np.array_equal(host(res.s_best).view(np.uint32), s_tab[best].view(np.uint32))
+    rng = np.random.default_rng(cfg * 10 + layer)
+    tm, tn = plan.tile_tokens, plan.tile_out
+    tiles = [(nt - 1, no - 1)] + [(int(rng.integers(nt)), int(rng.integers(no))) for _ in range(3)]
+    worst = 0.0
+    for (ti, oi) in tiles:
+        rows = slice(ti * tm, min((ti + 1) * tm, spec.n_tokens))
+        cols = slice(oi * tn, min((oi + 1) * tn, spec.out_features))
+        for i in (0, best, n_grid - 1):
+            want = O.tile_sq_error(X, W, s_tab[i], inv_s[i], rows, cols)
+            got = part[i, ti, oi]
+            worst = max(worst, abs(got - want) / want)
+            assert abs(got - want) <= LOSS_RTOL * want, (ti, oi, i, got, want)
+    # reference output X W^T at sampled positions
+    yref = ws[plan.yref_offset:plan.yref_offset + 4 * spec.n_tokens * spec.out_features] \
+        .view(torch.float32).view(spec.n_tokens, spec.out_features)
+    ti = rng.integers(0, spec.n_tokens, 64)
+    oi = rng.integers(0, spec.out_features, 64)
+    got = host(yref[torch.from_numpy(ti).cuda(), torch.from_numpy(oi).cuda()])
+    Xs = X[ti].astype(np.float64)
+    Ws = W[oi].astype(np.float64)
+    want = np.einsum("ij,ij->i", Xs, Ws)
+    scale = np.einsum("ij,ij->i", np.abs(Xs), np.abs(Ws))
+    assert np.all(np.abs(got - want) <= 1e-5 * scale + 1e-6)
+    _say(f"  worst sampled tile rel diff {worst:.3e}, best {best}")
