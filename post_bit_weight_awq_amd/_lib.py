@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libawq_mi355x.so")
+#: the in-tree library; AWQ_MI355X_LIB may name another build of the same sources
+LIB_PATH = os.environ.get("AWQ_MI355X_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libawq_mi355x.so")
 
 AWQ_OK = 0
 AWQ_ERR_INVALID_ARG = -1

@@ -12,10 +12,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq_mi355x.so")
-SOURCES = ["act_stats.hip", "search.hip", "pack.hip", "awq_api.hip"]
+SOURCES = ["act_stats.hip", "search.hip", "search_grid.hip", "pack.hip", "awq_api.hip"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     # no packed fp32 VALU ops anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # IEEE binary32 division and denormals: the codes depend on them
@@ -48,7 +48,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         cmd = [cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
-            cmd.insert(1, f"-save-temps={BUILD}" if False else "-save-temps")
+            cmd.insert(1, "-save-temps")
         objs.append(obj)
         cmds.append(cmd)
     cwd = os.getcwd()

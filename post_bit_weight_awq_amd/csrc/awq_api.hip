@@ -119,6 +119,9 @@ int awq_search_plan_query(int64_t n_tokens, int64_t in_features, int64_t out_fea
   if ((rc = check_dims(n_tokens, in_features, out_features, true, true, cfg->group_size))) return rc;
   if (!plan) return fail(AWQ_ERR_INVALID_ARG, "plan is NULL");
   const awq::SearchPlan p = awq::search_plan(n_tokens, in_features, out_features, cfg->n_grid);
+  if (p.grid_blocks > awq::kMaxGridBlocks)
+    return fail(AWQ_ERR_INVALID_ARG, "layer too large for one search launch (%lld tiles)",
+                (long long)(p.n_t_tiles * p.n_o_tiles));
   plan->tile_tokens = p.tile_m;
   plan->tile_out = p.tile_n;
   plan->n_token_tiles = p.n_t_tiles;
@@ -163,6 +166,9 @@ int awq_search_layer_stages(int stage_mask, const void* X, const void* W, const 
     return rc;
   if (!best_idx_out) return fail(AWQ_ERR_INVALID_ARG, "best_idx_out is NULL");
   const awq::SearchPlan p = awq::search_plan(n_tokens, in_features, out_features, cfg->n_grid);
+  if (p.grid_blocks > awq::kMaxGridBlocks)
+    return fail(AWQ_ERR_INVALID_ARG, "layer too large for one search launch (%lld tiles)",
+                (long long)(p.n_t_tiles * p.n_o_tiles));
   if (workspace_bytes < p.bytes)
     return fail(AWQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, p.bytes);
   return hip_result(awq::launch_search(X, W, sal, n_tokens, in_features, out_features,

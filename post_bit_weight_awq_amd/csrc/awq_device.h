@@ -32,6 +32,20 @@ __device__ __forceinline__ float mul_f16_f32(uint32_t w2, float s, float nz) {
   return r;
 }
 
+// The same with a wavefront-uniform scale held in a scalar register (saves the
+// copy into a vector register; at most one scalar operand per instruction).
+template <bool HI>
+__device__ __forceinline__ float mul_f16_f32_s(uint32_t w2, float s_uniform, float nz) {
+  float r;
+  if (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(w2), "s"(s_uniform), "v"(nz));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+        : "=v"(r) : "v"(w2), "s"(s_uniform), "v"(nz));
+  return r;
+}
+
 // Two fp16 values packed in one register: lo = fp16(a0 * b0), hi = fp16(a1 * b1),
 // each product of two fp32 values rounded ONCE (to nearest even) to fp16.
 __device__ __forceinline__ uint32_t mul_f32_to_f16x2(float a0, float b0, float a1, float b1,
@@ -44,12 +58,30 @@ __device__ __forceinline__ uint32_t mul_f32_to_f16x2(float a0, float b0, float a
   return r;
 }
 
+// As mul_f32_to_f16x2 with wavefront-uniform b0, b1 in scalar registers.
+__device__ __forceinline__ uint32_t mul_f32_to_f16x2_s(float a0, float b0_uniform, float a1,
+                                                       float b1_uniform, float nz) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]"
+      : "=v"(r) : "v"(a0), "s"(b0_uniform), "v"(nz));
+  asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel_hi:[0,0,0]"
+      : "+v"(r) : "v"(a1), "s"(b1_uniform), "v"(nz));
+  return r;
+}
+
 __device__ __forceinline__ float f16_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
 }
 __device__ __forceinline__ float f16_hi(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
+
+// Quantizer parameters of one (grid point, output row, group of 128):
+// step = (max - min) / 15, its binary32 reciprocal, and the clamp bounds of
+// (q - zero): lo = -zero, hi = 15 - zero.
+struct GroupParams {
+  float step, inv_step, lo, hi;
+};
 
 __device__ __forceinline__ float med3(float x, float lo, float hi) {
   return __builtin_amdgcn_fmed3f(x, lo, hi);

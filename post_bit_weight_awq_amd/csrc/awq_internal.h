@@ -7,6 +7,9 @@
 
 namespace awq {
 
+struct GroupParams;
+constexpr int kGridBN = 128;  // output features per grid-kernel tile
+
 struct StatsPlan {
   int64_t col_blocks;
   int64_t row_chunks;
@@ -21,6 +24,7 @@ struct SearchPlan {
   int64_t tile_m, tile_n;        // tokens x outputs per tile
   int64_t n_t_tiles, n_o_tiles;  // tile counts
   int kernel;                    // which tile kernel variant
+  int64_t grid_blocks;           // blocks of the grid-kernel launch
   size_t off_partials, off_yref, off_s, off_inv_s, off_params;
   size_t bytes;
 };
@@ -29,6 +33,14 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
                          int64_t in_features, int64_t out_features, int n_grid, float sal_floor,
                          double* losses, int32_t* best_idx, float* s_best, void* workspace,
                          const SearchPlan& plan, int stage_mask, hipStream_t stream);
+
+int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid);
+void launch_grid(int tile_m, bool ref, const void* X, const void* W, const float* s_tab,
+                 const float* inv_tab, const GroupParams* prm, float* yref, double* partials,
+                 int64_t N, int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid,
+                 hipStream_t stream);
+// largest grid the grid kernel is launched with (blocks of 256 threads in x)
+constexpr int64_t kMaxGridBlocks = (int64_t)1 << 23;
 
 hipError_t launch_pack(const void* W, const float* s, int64_t in_features, int64_t out_features,
                        int32_t* qweight, void* step16, void* zero16, hipStream_t stream);

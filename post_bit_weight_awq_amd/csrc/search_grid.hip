@@ -1,0 +1,359 @@
+// The fused grid kernel of the AWQ search: for one (grid point i, token tile,
+// output tile) it quantizes and dequantizes the weight tile of W diag(s_i)
+// (asymmetric INT4, groups of 128; "AWQ > Salient Weight Preservation",
+// step-size equation), divides it by s_i again (dev.to "AWQ: How
+// Activation-Aware Quantization Saves 4-bit LLMs", search_scale listing),
+// multiplies it with the activation tile on the MFMA units and reduces the
+// squared difference to the reference output X W^T over the tile in
+// registers.  The quantized output never leaves the chip.  The same kernel
+// with REF = true computes X W^T itself into the workspace.
+//
+// Layout (BM tokens x BN outputs per block, NW wavefronts, K steps of 32):
+//   * NW wavefronts stacked along tokens (8 for the 512- and 256-token tiles,
+//     two per SIMD, so one wavefront's loads and weight production overlap the
+//     other's MFMAs); each owns BM/NW tokens x BN outputs as 16x16 tiles of
+//     v_mfma_f32_16x16x32_f16, whose fp32 accumulators stay in registers for
+//     the whole K loop.
+//   * Activations go from global memory straight into each wavefront's
+//     A-fragment registers, one K step ahead (the other wavefront on the SIMD
+//     covers the latency).  The 16x16x32 fragment is 16
+//     rows x 64 contiguous bytes, so each load instruction touches 16 cache
+//     sectors: half as many as a 32x32 fragment, which matters because the
+//     vector data-return path, not bandwidth, limits these loads.
+//   * Weights take two LDS stages.  A coalesced load (four lanes per 64-byte
+//     row segment) lands the raw fp16 tile in LDS; then wavefront w turns the
+//     8-column chunk (w % 4) of rows (w / 4) * 64 + lane into the fake-
+//     quantized fp16 tile that all wavefronts read as B fragments.  The
+//     step's 32 scales and reciprocals travel with the raw tile into LDS and
+//     are read as wavefront-wide broadcasts (no scalar loads in the loop:
+//     they would share the LDS wait counter and force full drains); each
+//     row's group parameters load once per 128 columns.
+//     The production cost is spread over the BM tokens of the tile.
+//   * Pipeline at K step q: MFMAs on (A(q), Wq(q)), interleaved one MFMA to
+//     two VALU instructions with producing Wq(q+1) from raw W(q+1); store raw
+//     W(q+2) (loaded one step earlier); load raw W(q+3) and A(q+1).  Every
+//     stage is double-buffered; one barrier per step.  The 512-token tile
+//     gives each wavefront 32 MFMAs per step, enough to hide the production.
+//   * Operand k mapping: lane l holds k0 + 8*(l/16) .. +7 of row (l % 16) for
+//     both A (tokens) and B (outputs), so each MFMA sums matching k pairs.
+//     Accumulator register r of lane l holds C[4*(l/16) + r][l % 16].
+//   * Block order: linear block b runs on XCD b % 8.  The j-th block an XCD
+//     receives takes grid point j % n_grid of tile 8*(j / n_grid) + xcd, so
+//     the blocks resident on one XCD at a time are the grid points of one or
+//     two tiles and share the tiles' activation and weight rows in that XCD's L2.
+#include "awq_device.h"
+#include "awq_internal.h"
+
+namespace awq {
+
+template <int BM, int BN, int NW, bool REF>
+__global__ void __launch_bounds__(NW * 64, 1)
+k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
+       const float* __restrict__ s_tab, const float* __restrict__ inv_tab,
+       const GroupParams* __restrict__ prm, float* __restrict__ yref,
+       double* __restrict__ partials, int N, int K, int OUT, int n_t_tiles, int n_o_tiles,
+       int n_grid) {
+  constexpr int NT = NW * 64;
+  constexpr int KC = 32;            // k per step (one 16x16x32 MFMA deep)
+  constexpr int WMT = BM / NW;      // tokens per wavefront
+  constexpr int MBW = WMT / 16;     // 16-row MFMA tiles per wavefront
+  constexpr int NBW = BN / 16;      // 16-column MFMA tiles
+  constexpr int NH = NBW / 2;       // B fragments are read in two halves
+  constexpr int LDW = KC + 8;       // LDS row stride (halves): conflict-free 16-byte reads
+  constexpr int PR = BN * 4 / NT;   // raw rows stored and produced per thread per step
+  static_assert(MBW >= 1 && NBW % 2 == 0 && PR >= 1 && WMT % 16 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) _Float16 wq[2][BN * LDW];   // fake-quantized
+  __shared__ __attribute__((aligned(16))) _Float16 wraw[2][BN * LDW]; // raw fp16 weights
+  __shared__ __attribute__((aligned(16))) float scl[2][2 * KC];       // s | 1/s of a step
+  __shared__ double red[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_items = REF ? 1 : n_grid;
+  const int n_tiles = n_t_tiles * n_o_tiles;
+  const int jb = blockIdx.x >> 3;
+  const int ai = jb % n_items;
+  const int T = (jb / n_items) * 8 + (blockIdx.x & 7);
+  if (T >= n_tiles) return;
+  const int tt = T / n_o_tiles, ot = T - tt * n_o_tiles;
+  const int t0 = tt * BM, o0 = ot * BN;
+  const int ngroups = K >> 7;
+  const int nk = K / KC;  // a multiple of 4
+  const float nz = neg_zero();
+
+  // activation rows of this lane, as 32-bit offsets from the tile's first row
+  // (rows past the end re-read the last row; their outputs are masked in the
+  // epilogue)
+  const _Float16* xt = X + (size_t)t0 * K;
+  uint32_t pa[MBW];
+#pragma unroll
+  for (int m = 0; m < MBW; ++m) {
+    const int row = min(t0 + wave * WMT + m * 16 + (lane & 15), N - 1) - t0;
+    pa[m] = (uint32_t)row * (uint32_t)K + 8 * (lane >> 4);
+  }
+  // coalesced raw-weight loads: thread t covers 16 bytes of row t/4 (+ NT/4 j),
+  // as 32-bit offsets from the tile's first row
+  const _Float16* wt = W + (size_t)o0 * K;
+  uint32_t pwl[PR];
+#pragma unroll
+  for (int j = 0; j < PR; ++j) {
+    const int go = min(o0 + (tid >> 2) + (NT / 4) * j, OUT - 1) - o0;
+    pwl[j] = (uint32_t)go * (uint32_t)K + 8 * (tid & 3);
+  }
+  // production: the wavefront-uniform chunk pc of rows prow0 + (NT/4) j
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int pc = wv & 3;
+  const int prow0 = (wv >> 2) * 64 + lane;
+  // parameters, layout [grid point][group][row]: uniform base + row offset
+  const GroupParams* pt = prm + (size_t)ai * ngroups * OUT + o0;
+  uint32_t pp[PR];
+#pragma unroll
+  for (int j = 0; j < PR; ++j) pp[j] = (uint32_t)(min(o0 + prow0 + (NT / 4) * j, OUT - 1) - o0);
+  // scale staging: threads 0..15 copy the step's 32 scales and 32 reciprocals
+  const float* pst = s_tab + (size_t)ai * K;
+  const float* pit = inv_tab + (size_t)ai * K;
+
+  floatx4 acc[MBW][NBW];
+#pragma unroll
+  for (int m = 0; m < MBW; ++m)
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) acc[m][n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Pipeline state is held in small by-value structs with fixed names (no
+  // arrays indexed by step parity), so every stage stays in registers.
+  struct AF {
+    half8 v[MBW];  // activation fragments of one step
+  };
+  struct WR {
+    uint4 v[PR];   // raw weights of one step, in flight
+    float4 sc;     // threads 0..15: four of the step's scales or reciprocals
+  };
+  auto load_a = [&](int step) {
+    AF r;
+#pragma unroll
+    for (int m = 0; m < MBW; ++m) r.v[m] = *(const half8*)(xt + pa[m] + step * KC);
+    return r;
+  };
+  auto load_w = [&](int step) {
+    WR r;
+#pragma unroll
+    for (int j = 0; j < PR; ++j) r.v[j] = *(const uint4*)(wt + pwl[j] + step * KC);
+    if (!REF && tid < 16)
+      r.sc = *(const float4*)((tid < 8 ? pst : pit) + 4 * (tid & 7) + step * KC);
+    return r;
+  };
+  auto store_raw = [&](int buf, WR src) {
+#pragma unroll
+    for (int j = 0; j < PR; ++j)
+      *(uint4*)(&wraw[buf][((tid >> 2) + (NT / 4) * j) * LDW + 8 * (tid & 3)]) = src.v[j];
+    if (!REF && tid < 16) *(float4*)(&scl[buf][(tid < 8 ? 0 : KC) + 4 * (tid & 7)]) = src.sc;
+  };
+  // group parameters as float4: x = step, y = 1/step, z = -zero, w = 15 - zero
+  struct GP {
+    float4 v[PR];
+  };
+  auto load_params = [&](int grp) {
+    GP g;
+    if (!REF) {
+#pragma unroll
+      for (int j = 0; j < PR; ++j) g.v[j] = *(const float4*)(pt + pp[j] + (size_t)grp * OUT);
+    }
+    return g;
+  };
+  // Wq(step) from raw buffer `buf` (weights and the step's scales) into LDS
+  // buffer `buf`; the wavefront's 8 scales are broadcast reads
+  auto produce = [&](int buf, GP gp) {
+    float sv[8], iv[8];
+    if (!REF) {
+      const float4 s0 = *(const float4*)(&scl[buf][8 * pc]);
+      const float4 s1 = *(const float4*)(&scl[buf][8 * pc + 4]);
+      const float4 i0 = *(const float4*)(&scl[buf][KC + 8 * pc]);
+      const float4 i1 = *(const float4*)(&scl[buf][KC + 8 * pc + 4]);
+      sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
+      sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+      iv[0] = i0.x; iv[1] = i0.y; iv[2] = i0.z; iv[3] = i0.w;
+      iv[4] = i1.x; iv[5] = i1.y; iv[6] = i1.z; iv[7] = i1.w;
+    }
+#pragma unroll
+    for (int j = 0; j < PR; ++j) {
+      const int row = prow0 + (NT / 4) * j;
+      const uint4 r = *(const uint4*)(&wraw[buf][row * LDW + 8 * pc]);
+      uint4 out = r;
+      if (!REF) {
+        const float4 g = gp.v[j];
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float fa = mul_f16_f32<false>(w[e], sv[2 * e], nz);
+          const float fb = mul_f16_f32<true>(w[e], sv[2 * e + 1], nz);
+          const float ca = med3(rintf(fa * g.y), g.z, g.w) * g.x;
+          const float cb = med3(rintf(fb * g.y), g.z, g.w) * g.x;
+          o[e] = mul_f32_to_f16x2(ca, iv[2 * e], cb, iv[2 * e + 1], nz);
+        }
+        out = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+      *(uint4*)(&wq[buf][row * LDW + 8 * pc]) = out;
+    }
+  };
+  auto mfma_half = [&](const AF& av, int buf, int h) {
+    half8 bf[NH];
+#pragma unroll
+    for (int n = 0; n < NH; ++n)
+      bf[n] = *(const half8*)(&wq[buf][((h * NH + n) * 16 + (lane & 15)) * LDW + 8 * (lane >> 4)]);
+#pragma unroll
+    for (int m = 0; m < MBW; ++m)
+#pragma unroll
+      for (int n = 0; n < NH; ++n)
+        acc[m][h * NH + n] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(av.v[m], bf[n], acc[m][h * NH + n], 0, 0, 0);
+  };
+  // one K step: MFMAs on `cur` and Wq buffer `buf`, interleaved with producing
+  // Wq(step+1) into the other buffer; then the raw store of `wst` into raw
+  // buffer `buf` and a barrier.  The scheduler is asked for one MFMA, then two
+  // VALU instructions, repeated: with two wavefronts per SIMD the production
+  // work then runs under the MFMA pipeline instead of after it.
+  auto step_body = [&](const AF& cur, int buf, GP gprod, WR wst) {
+    mfma_half(cur, buf, 0);
+    produce(buf ^ 1, gprod);
+    mfma_half(cur, buf, 1);
+    store_raw(buf, wst);
+#pragma unroll
+    for (int i = 0; i < MBW * NBW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+    __syncthreads();
+  };
+
+  // Pipeline at step q: MFMAs on A(q) and Wq(q) (LDS buffer q % 2),
+  // interleaved with producing Wq(q+1) from raw W(q+1); store raw W(q+2)
+  // (loaded during step q-1) into raw buffer q % 2; load raw W(q+3) and
+  // A(q+1).  Loads past the last step re-read step nk - 1 (never used), which
+  // keeps the body branch-free and every wait count exact.
+  GP gcur = load_params(0);
+  GP gnxt = load_params(min(1, ngroups - 1));
+  WR w = load_w(0);
+  store_raw(0, w);
+  w = load_w(1);
+  store_raw(1, w);
+  w = load_w(min(2, nk - 1));
+  AF a0 = load_a(0), a1;
+  __syncthreads();
+  produce(0, gcur);
+  __syncthreads();
+  for (int gi = 0; gi < ngroups; ++gi) {
+    const int q = 4 * gi;
+    a1 = load_a(q + 1);
+    step_body(a0, 0, gcur, w);  // produces Wq(q+1) from raw buffer 1
+    w = load_w(min(q + 3, nk - 1));
+    a0 = load_a(q + 2);
+    step_body(a1, 1, gcur, w);
+    w = load_w(min(q + 4, nk - 1));
+    a1 = load_a(q + 3);
+    step_body(a0, 0, gcur, w);
+    w = load_w(min(q + 5, nk - 1));
+    a0 = load_a(min(q + 4, nk - 1));
+    step_body(a1, 1, gnxt, w);  // Wq(q+4): first step of the next group
+    w = load_w(min(q + 6, nk - 1));
+    gcur = gnxt;
+    gnxt = load_params(min(gi + 2, ngroups - 1));
+  }
+
+  // epilogue
+  const int tb = t0 + wave * WMT + 4 * (lane >> 4);
+  const int oc = o0 + (lane & 15);
+  if (REF) {
+#pragma unroll
+    for (int m = 0; m < MBW; ++m)
+#pragma unroll
+      for (int n = 0; n < NBW; ++n) {
+        const int o = oc + n * 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tb + m * 16 + r;
+          if (t < N && o < OUT) yref[(size_t)t * OUT + o] = acc[m][n][r];
+        }
+      }
+    return;
+  }
+  double dsum = 0.0;
+#pragma unroll
+  for (int m = 0; m < MBW; ++m) {
+    float sq = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) {
+      const int o = oc + n * 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb + m * 16 + r;
+        if (t < N && o < OUT) {
+          const float d = acc[m][n][r] - yref[(size_t)t * OUT + o];
+          sq = fmaf(d, d, sq);
+        }
+      }
+    }
+    dsum += (double)sq;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) dsum += __shfl_xor(dsum, d, kWave);
+  if (lane == 0) red[wave] = dsum;
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += red[w];
+    partials[(size_t)ai * n_tiles + T] = tot;
+  }
+}
+
+int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
+  // Largest token tile whose block count still fills the chip a few times
+  // over; larger tiles spread the weight producer over more tokens and read
+  // less from L2 per MFMA.
+  const int64_t o_tiles = (out_features + kGridBN - 1) / kGridBN;
+  for (int bm : {512, 256}) {
+    const int64_t blocks = (n_tokens + bm - 1) / bm * o_tiles * n_grid;
+    if (blocks >= 4 * 256) return bm;
+  }
+  return 128;
+}
+
+template <int BM, int NW>
+static void launch_one(bool ref, dim3 grid, hipStream_t stream, const _Float16* X,
+                       const _Float16* W, const float* s_tab, const float* inv_tab,
+                       const GroupParams* prm, float* yref, double* partials, int N, int K,
+                       int OUT, int nt, int no, int n_grid) {
+  if (ref)
+    hipLaunchKernelGGL((k_grid<BM, kGridBN, NW, true>), grid, dim3(NW * 64), 0, stream, X, W, s_tab,
+                       inv_tab, prm, yref, partials, N, K, OUT, nt, no, n_grid);
+  else
+    hipLaunchKernelGGL((k_grid<BM, kGridBN, NW, false>), grid, dim3(NW * 64), 0, stream, X, W, s_tab,
+                       inv_tab, prm, yref, partials, N, K, OUT, nt, no, n_grid);
+}
+
+void launch_grid(int tile_m, bool ref, const void* X, const void* W, const float* s_tab,
+                 const float* inv_tab, const GroupParams* prm, float* yref, double* partials,
+                 int64_t N, int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid,
+                 hipStream_t stream) {
+  const int64_t items = ref ? 1 : n_grid;
+  const int64_t tiles8 = (nt * no + 7) / 8 * 8;
+  const dim3 grid((unsigned)(tiles8 * items));
+  const _Float16* Xh = (const _Float16*)X;
+  const _Float16* Wh = (const _Float16*)W;
+  switch (tile_m) {
+    case 512:
+      launch_one<512, 8>(ref, grid, stream, Xh, Wh, s_tab, inv_tab, prm, yref, partials, (int)N,
+                         (int)K, (int)OUT, (int)nt, (int)no, n_grid);
+      break;
+    case 256:
+      launch_one<256, 8>(ref, grid, stream, Xh, Wh, s_tab, inv_tab, prm, yref, partials, (int)N,
+                         (int)K, (int)OUT, (int)nt, (int)no, n_grid);
+      break;
+    default:
+      launch_one<128, 4>(ref, grid, stream, Xh, Wh, s_tab, inv_tab, prm, yref, partials, (int)N,
+                         (int)K, (int)OUT, (int)nt, (int)no, n_grid);
+      break;
+  }
+}
+
+}  // namespace awq
