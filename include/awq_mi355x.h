@@ -105,8 +105,11 @@ int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* s
  *   s_best_out:   [in_features] fp32: s_i* (all NaN when i* = -1)
  *   in_features must be a multiple of group_size; n_tokens, out_features >= 1.
  * The workspace (size from awq_search_workspace_size) holds the scale table,
- * the per-group quantizer parameters, the reference output X W^T in fp32 and
- * the per-tile partial sums; awq_search_plan describes where.
+ * the per-group quantizer parameters and the per-tile partial sums;
+ * awq_search_plan describes where.  The squared output error is formed as
+ * (X (Wq - W)^T)^2 with the weight error rounded once to fp16 (the same
+ * quantity as (X Wq^T - X W^T)^2 up to that rounding), so no reference output
+ * is stored.
  * Source: dev.to page, search_scale listing; Salient Weight Preservation page,
  * step-size equation.
  * ---------------------------------------------------------------------- */
@@ -117,7 +120,6 @@ typedef struct awq_search_plan {
   int64_t n_out_tiles;     /* ceil(out_features / tile_out)                        */
   size_t partials_offset;  /* double [n_grid][n_token_tiles][n_out_tiles]: sum of
                               squared differences over each tile (not averaged)   */
-  size_t yref_offset;      /* float [n_tokens][out_features]: X W^T                */
   size_t scales_offset;    /* float [n_grid][in_features]: s_i                     */
   size_t workspace_bytes;  /* total workspace size                                 */
 } awq_search_plan;

@@ -35,8 +35,8 @@ class AwqConfig(ctypes.Structure):
 class AwqSearchPlan(ctypes.Structure):
     _fields_ = [("tile_tokens", ctypes.c_int64), ("tile_out", ctypes.c_int64),
                 ("n_token_tiles", ctypes.c_int64), ("n_out_tiles", ctypes.c_int64),
-                ("partials_offset", ctypes.c_size_t), ("yref_offset", ctypes.c_size_t),
-                ("scales_offset", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t)]
+                ("partials_offset", ctypes.c_size_t), ("scales_offset", ctypes.c_size_t),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 class AwqError(RuntimeError):

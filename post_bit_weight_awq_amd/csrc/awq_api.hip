@@ -127,7 +127,6 @@ int awq_search_plan_query(int64_t n_tokens, int64_t in_features, int64_t out_fea
   plan->n_token_tiles = p.n_t_tiles;
   plan->n_out_tiles = p.n_o_tiles;
   plan->partials_offset = p.off_partials;
-  plan->yref_offset = p.off_yref;
   plan->scales_offset = p.off_s;
   plan->workspace_bytes = p.bytes;
   return ok();

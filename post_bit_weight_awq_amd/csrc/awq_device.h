@@ -69,6 +69,13 @@ __device__ __forceinline__ uint32_t mul_f32_to_f16x2_s(float a0, float b0_unifor
   return r;
 }
 
+// Packed fp16 a - b, each half rounded once (IEEE, to nearest even).
+__device__ __forceinline__ uint32_t sub_f16x2(uint32_t a, uint32_t b) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const half2v r = __builtin_bit_cast(half2v, a) - __builtin_bit_cast(half2v, b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 __device__ __forceinline__ float f16_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
 }

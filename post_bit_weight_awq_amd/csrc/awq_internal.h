@@ -25,7 +25,7 @@ struct SearchPlan {
   int64_t n_t_tiles, n_o_tiles;  // tile counts
   int kernel;                    // which tile kernel variant
   int64_t grid_blocks;           // blocks of the grid-kernel launch
-  size_t off_partials, off_yref, off_s, off_inv_s, off_params;
+  size_t off_partials, off_s, off_inv_s, off_params;
   size_t bytes;
 };
 SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid);
@@ -35,10 +35,9 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
                          const SearchPlan& plan, int stage_mask, hipStream_t stream);
 
 int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid);
-void launch_grid(int tile_m, bool ref, const void* X, const void* W, const float* s_tab,
-                 const float* inv_tab, const GroupParams* prm, float* yref, double* partials,
-                 int64_t N, int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid,
-                 hipStream_t stream);
+void launch_grid(int tile_m, const void* X, const void* W, const float* s_tab,
+                 const float* inv_tab, const GroupParams* prm, double* partials, int64_t N,
+                 int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream);
 // largest grid the grid kernel is launched with (blocks of 256 threads in x)
 constexpr int64_t kMaxGridBlocks = (int64_t)1 << 23;
 

@@ -12,12 +12,12 @@
 // Kernels, in launch order:
 //   k_scale_table   s[i,k] = fp32(pow(fp64 max(sal_k, floor), i/n)), inv_s = fp32(1/s)
 //   k_group_params  per (i, group, row): step, 1/step, -zero, 15-zero of W diag(s_i)
-//   k_grid<REF>     reference output X W^T (fp32, into the workspace)
-//   k_grid<SEARCH>  per (i, token tile, output tile): builds the fake-quantized
-//                   fp16 weight tile in LDS, contracts it with the activation tile
-//                   on the MFMA units (fp16 x fp16 -> fp32), and reduces
-//                   (Y_q - Y_ref)^2 over the tile in registers; Y_q never leaves
-//                   the chip.  One partial sum per tile (search_grid.hip).
+//   k_grid          per (i, token tile, output tile): builds the fp16 weight-error
+//                   tile fp16(Wq - W) in LDS, contracts it with the activation tile
+//                   on the MFMA units (fp16 x fp16 -> fp32), which gives
+//                   Y_q - Y_ref = X (Wq - W)^T directly, and reduces its square
+//                   over the tile in registers; no output ever leaves the chip.
+//                   One partial sum per tile (search_grid.hip).
 //   k_argmin        fixed-order sum of the partials per grid point, mean, and a
 //                   wavefront-shuffle argmin (lowest index wins ties).
 #include "awq_device.h"
@@ -176,8 +176,6 @@ SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_featur
   size_t off = 0;
   p.off_partials = off;
   off = align256(off + sizeof(double) * (size_t)n_grid * p.n_t_tiles * p.n_o_tiles);
-  p.off_yref = off;
-  off = align256(off + sizeof(float) * (size_t)n_tokens * out_features);
   p.off_s = off;
   off = align256(off + sizeof(float) * (size_t)n_grid * in_features);
   p.off_inv_s = off;
@@ -194,7 +192,6 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
                          int stage_mask, hipStream_t stream) {
   char* ws = (char*)workspace;
   double* partials = (double*)(ws + p.off_partials);
-  float* yref = (float*)(ws + p.off_yref);
   float* s_tab = (float*)(ws + p.off_s);
   float* inv_tab = (float*)(ws + p.off_inv_s);
   GroupParams* prm = (GroupParams*)(ws + p.off_params);
@@ -206,12 +203,10 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
                        sal, s_tab, inv_tab, K, n_grid, sal_floor);
     hipLaunchKernelGGL(k_group_params, dim3((unsigned)((OUT + 63) / 64), (unsigned)ng), dim3(256),
                        0, stream, (const _Float16*)W, s_tab, prm, (int)OUT, (int)K, n_grid);
-    launch_grid((int)p.tile_m, true, X, W, s_tab, inv_tab, prm, yref, partials, N, K, OUT,
-                p.n_t_tiles, p.n_o_tiles, n_grid, stream);
   }
   if (stage_mask & 2) {  // grid
-    launch_grid((int)p.tile_m, false, X, W, s_tab, inv_tab, prm, yref, partials, N, K, OUT,
-                p.n_t_tiles, p.n_o_tiles, n_grid, stream);
+    launch_grid((int)p.tile_m, X, W, s_tab, inv_tab, prm, partials, N, K, OUT, p.n_t_tiles,
+                p.n_o_tiles, n_grid, stream);
   }
   if (stage_mask & 4) {  // select
     hipLaunchKernelGGL(k_argmin, dim3(1), dim3(kArgminThreads), 0, stream, partials,

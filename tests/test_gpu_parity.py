@@ -7,8 +7,8 @@ Bars (element by element, same seeded inputs on both sides):
   * chosen index: identical unless the oracle's two best losses lie within
     1e-3 relative of each other; s_best bit-exact against the oracle's s row;
   * full-size layers: per-tile partial sums of sampled tiles within 1e-3
-    relative of the oracle's block sums, sampled X W^T values within fp32
-    accumulation error, and the loss/argmin consistent with those partials.
+    relative of the oracle's block sums, and the loss/argmin consistent with
+    those partials.
 """
 import os
 import sys
@@ -257,15 +257,4 @@ def test_full_size_layer_sampled_tiles(awq, cfg, layer):
             got = part[i, ti, oi]
             worst = max(worst, abs(got - want) / want)
             assert abs(got - want) <= LOSS_RTOL * want, (ti, oi, i, got, want)
-    # reference output X W^T at sampled positions
-    yref = ws[plan.yref_offset:plan.yref_offset + 4 * spec.n_tokens * spec.out_features] \
-        .view(torch.float32).view(spec.n_tokens, spec.out_features)
-    ti = rng.integers(0, spec.n_tokens, 64)
-    oi = rng.integers(0, spec.out_features, 64)
-    got = host(yref[torch.from_numpy(ti).cuda(), torch.from_numpy(oi).cuda()])
-    Xs = X[ti].astype(np.float64)
-    Ws = W[oi].astype(np.float64)
-    want = np.einsum("ij,ij->i", Xs, Ws)
-    scale = np.einsum("ij,ij->i", np.abs(Xs), np.abs(Ws))
-    assert np.all(np.abs(got - want) <= 1e-5 * scale + 1e-6)
     _say(f"  worst sampled tile rel diff {worst:.3e}, best {best}")
