@@ -296,7 +296,7 @@ int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
   const int64_t o_tiles = (out_features + kGridBN - 1) / kGridBN;
   for (int bm : {512, 256}) {
     const int64_t blocks = (n_tokens + bm - 1) / bm * o_tiles * n_grid;
-    if (blocks >= 4 * 256) return bm;
+    if (blocks >= 2 * 256) return bm;
   }
   return 128;
 }
