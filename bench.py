@@ -55,7 +55,7 @@ def pack_bytes(spec):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("search.hip", "awq_device.h"):
+    for f in ("search_grid.hip", "awq_device.h"):
         h.update(open(os.path.join(ROOT, "post_bit_weight_awq_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -263,7 +263,7 @@ def main():
             {"name": L["spec"].name, "n_tokens": L["spec"].n_tokens,
              "in_features": L["spec"].in_features, "out_features": L["spec"].out_features}
             for L in layers], "group_size": 128, "w_bit": 4, "n_grid": cfg.n_grid},
-        "roofline": {"bound": "mfma", "kernel": "k_tile (fused grid search)",
+        "roofline": {"bound": "mfma", "kernel": "k_grid (fused alpha-grid search)",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": traffic,

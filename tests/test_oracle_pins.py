@@ -99,6 +99,31 @@ def test_losses_match_exact_rationals(seed):
         assert res.losses[i] == pytest.approx(float(exact), rel=1e-12, abs=0)
 
 
+def test_tile_squared_error_matches_exact_rationals():
+    """The per-block squared error that full-size parity samples: each block
+    equals the exact rational sum over that block, and the blocks of a
+    partition add up to the layer loss times its element count."""
+    X, W = _tiny_case(5, n=7, k=256, out=5)
+    sal = O.act_stats(X)
+    res = O.search_layer(X, W, sal)
+    Xf = [[Fraction(float(v)) for v in row] for row in X]
+    Wf = [[Fraction(float(v)) for v in row] for row in W]
+    rows_parts = [slice(0, 3), slice(3, 7)]
+    cols_parts = [slice(0, 2), slice(2, 5)]
+    for i in (0, 11, 19):
+        s_fr = [Fraction(float(v)) for v in res.s[i]]
+        Wq = [brute.fake_quant_row(row, s_fr)[0] for row in Wf]
+        total = 0.0
+        for rs in rows_parts:
+            for cs in cols_parts:
+                got = O.tile_sq_error(X, W, res.s[i], res.inv_s[i], rs, cs)
+                n_el = (rs.stop - rs.start) * (cs.stop - cs.start)
+                exact = brute.mse_exact(Xf[rs], Wf[cs], Wq[cs]) * n_el
+                assert got == pytest.approx(float(exact), rel=1e-12, abs=0)
+                total += got
+        assert total == pytest.approx(res.losses[i] * X.shape[0] * W.shape[0], rel=1e-12)
+
+
 def test_stats_exact_mean_then_two_roundings():
     rng = np.random.default_rng(7)
     X = (rng.standard_normal((37, 64)) * 50).astype(F16)
