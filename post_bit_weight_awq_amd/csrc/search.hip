@@ -44,32 +44,66 @@ k_scale_table(const float* __restrict__ sal, float* __restrict__ s_tab,
 // ------------------------------------------------- per-group quantizer params
 // A team of 4 lanes owns one (row, group of 128); each lane holds 32 of the
 // group's weights for the whole grid loop.  The 16 teams of a wavefront share
-// the group and take consecutive rows, so they read the same scale row and
-// write consecutive parameter records (layout [grid point][group][row]).
+// the group and take consecutive rows; a block covers 64 rows.  The block first
+// copies the group's scales for every grid point into LDS (one coalesced pass
+// over the scale table), so the grid loop only reads LDS.
 // Per grid point: ws = fp32(w s), min and max over the group, then
 // step = (max - min) / 15 with IEEE division (1 for a zero range),
 // zero = rint(-min / step) (+0 for a zero), 1/step, and the clamp bounds.
-__device__ __forceinline__ float quad_min(float x) {
-  x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
-  x = fminf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
-  return x;
+// Grid points go in blocks of four: after the team's min/max reductions every
+// lane of the team holds all four (min, max) pairs, and lane j of the team
+// finishes grid point i0 + j, so the three divisions run on all lanes at once.
+// Records are written in the layout [grid point][group][row].
+constexpr int kParamsRows = 64;
+// LDS copy of one grid point's 128 scales: four 32-float chunks (one per team
+// lane), each padded by 4 floats so the four chunks a wavefront reads at once
+// sit in different banks.
+constexpr int kParamsChunk = 36;
+constexpr int kParamsPerGrid = 4 * kParamsChunk;
+
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
-__device__ __forceinline__ float quad_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
-  return x;
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// min / max with a lane of the same quad (DPP quad permutation CTRL).  The
+// operations are written out (min3/max3 above) because the compiler's own
+// min/max would first canonicalize operands it cannot prove canonical.
+template <int CTRL>
+__device__ __forceinline__ float quad_min_step(float x) {
+  const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+  return min3f(x, y, y);
+}
+template <int CTRL>
+__device__ __forceinline__ float quad_max_step(float x) {
+  const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+  return max3f(x, y, y);
 }
 
 __global__ void __launch_bounds__(256)
 k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
                GroupParams* __restrict__ prm, int OUT, int K, int n_grid) {
+  extern __shared__ float4 s_lds4[];  // [n_grid][4 chunks][9 float4]
   const int ngroups = K >> 7;
   const int g = blockIdx.y;
-  const int l4 = threadIdx.x & 3;
-  const int o_raw = blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int tid = threadIdx.x;
+  const int l4 = tid & 3;
+  const int o_raw = blockIdx.x * kParamsRows + (tid >> 2);
   const bool live = o_raw < OUT;
   const int o = live ? o_raw : OUT - 1;
   const int k0 = g * kGroup + l4 * 32;
+
+  // scales of this group, every grid point: element e = (i, 16-byte column c4)
+  for (int e = tid; e < n_grid * 32; e += 256) {
+    const int i = e >> 5, c4 = e & 31;
+    const float4 v = ((const float4*)(s_tab + (size_t)i * K + g * kGroup))[c4];
+    s_lds4[i * (kParamsPerGrid / 4) + (c4 >> 3) * (kParamsChunk / 4) + (c4 & 7)] = v;
+  }
   const uint4* wp = (const uint4*)(W + (size_t)o * K + k0);
   uint32_t w[16];
 #pragma unroll
@@ -80,23 +114,53 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     w[4 * v + 2] = t.z;
     w[4 * v + 3] = t.w;
   }
+  __syncthreads();
   const float nz = neg_zero();
-  for (int i = 0; i < n_grid; ++i) {
-    const float4* sp = (const float4*)(s_tab + (size_t)i * K + k0);
-    float mn = INFINITY, mx = -INFINITY;
+  for (int i0 = 0; i0 < n_grid; i0 += 4) {
+    float mnv[4], mxv[4];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const float4 sv = sp[v];
-      const float a = mul_f16_f32<false>(w[2 * v], sv.x, nz);
-      const float b = mul_f16_f32<true>(w[2 * v], sv.y, nz);
-      const float c = mul_f16_f32<false>(w[2 * v + 1], sv.z, nz);
-      const float d = mul_f16_f32<true>(w[2 * v + 1], sv.w, nz);
-      mn = fminf(mn, fminf(fminf(a, b), fminf(c, d)));
-      mx = fmaxf(mx, fmaxf(fmaxf(a, b), fmaxf(c, d)));
+    for (int j = 0; j < 4; ++j) {
+      const int i = min(i0 + j, n_grid - 1);
+      const float4* sp = s_lds4 + i * (kParamsPerGrid / 4) + l4 * (kParamsChunk / 4);
+      float mn, mx;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float4 sv = sp[v];
+        const float a = mul_f16_f32<false>(w[2 * v], sv.x, nz);
+        const float b = mul_f16_f32<true>(w[2 * v], sv.y, nz);
+        const float c = mul_f16_f32<false>(w[2 * v + 1], sv.z, nz);
+        const float d = mul_f16_f32<true>(w[2 * v + 1], sv.w, nz);
+        if (v == 0) {
+          mn = min3f(a, b, c);
+          mx = max3f(a, b, c);
+          mn = min3f(mn, d, d);
+          mx = max3f(mx, d, d);
+        } else {
+          mn = min3f(mn, a, b);
+          mx = max3f(mx, a, b);
+          mn = min3f(mn, c, d);
+          mx = max3f(mx, c, d);
+        }
+      }
+      mnv[j] = mn;
+      mxv[j] = mx;
     }
-    mn = quad_min(mn);
-    mx = quad_max(mx);
-    if (live && l4 == 0) {
+    // team reductions, all eight values per DPP step (keeps DPP reads away
+    // from the writes they depend on)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mnv[j] = quad_min_step<0xB1>(mnv[j]);
+      mxv[j] = quad_max_step<0xB1>(mxv[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mnv[j] = quad_min_step<0x4E>(mnv[j]);
+      mxv[j] = quad_max_step<0x4E>(mxv[j]);
+    }
+    const float mn = l4 == 0 ? mnv[0] : l4 == 1 ? mnv[1] : l4 == 2 ? mnv[2] : mnv[3];
+    const float mx = l4 == 0 ? mxv[0] : l4 == 1 ? mxv[1] : l4 == 2 ? mxv[2] : mxv[3];
+    const int i = i0 + l4;
+    if (live && i < n_grid) {
       float step = (mx - mn) / 15.0f;
       if (step == 0.0f) step = 1.0f;
       const float z = rintf(-mn / step) + 0.0f;
@@ -109,6 +173,8 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     }
   }
 }
+
+size_t group_params_lds_bytes(int n_grid) { return sizeof(float) * kParamsPerGrid * n_grid; }
 
 // -------------------------------------------------------------------- argmin
 // 1024 threads: wavefront w sums the partials of grid points w, w+16, ... in
@@ -201,8 +267,10 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
     const int64_t nst = (int64_t)n_grid * K;
     hipLaunchKernelGGL(k_scale_table, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, stream,
                        sal, s_tab, inv_tab, K, n_grid, sal_floor);
-    hipLaunchKernelGGL(k_group_params, dim3((unsigned)((OUT + 63) / 64), (unsigned)ng), dim3(256),
-                       0, stream, (const _Float16*)W, s_tab, prm, (int)OUT, (int)K, n_grid);
+    hipLaunchKernelGGL(k_group_params,
+                       dim3((unsigned)((OUT + kParamsRows - 1) / kParamsRows), (unsigned)ng),
+                       dim3(256), group_params_lds_bytes(n_grid), stream, (const _Float16*)W,
+                       s_tab, prm, (int)OUT, (int)K, n_grid);
   }
   if (stage_mask & 2) {  // grid
     launch_grid((int)p.tile_m, X, W, s_tab, inv_tab, prm, partials, N, K, OUT, p.n_t_tiles,
