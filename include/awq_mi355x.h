@@ -118,8 +118,9 @@ typedef struct awq_search_plan {
   int64_t tile_out;        /* output features per output tile                      */
   int64_t n_token_tiles;   /* ceil(n_tokens / tile_tokens)                         */
   int64_t n_out_tiles;     /* ceil(out_features / tile_out)                        */
-  size_t partials_offset;  /* double [n_grid][n_token_tiles][n_out_tiles]: sum of
-                              squared differences over each tile (not averaged)   */
+  size_t partials_offset;  /* double [n_grid][n_token_tiles][n_out_tiles][2]: the
+                              sum of squared differences over a tile (not
+                              averaged) is the sum of its two entries            */
   size_t scales_offset;    /* float [n_grid][in_features]: s_i                     */
   size_t workspace_bytes;  /* total workspace size                                 */
 } awq_search_plan;

@@ -241,7 +241,7 @@ SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_featur
   p.grid_blocks = (p.n_t_tiles * p.n_o_tiles + 7) / 8 * 8 * n_grid;
   size_t off = 0;
   p.off_partials = off;
-  off = align256(off + sizeof(double) * (size_t)n_grid * p.n_t_tiles * p.n_o_tiles);
+  off = align256(off + sizeof(double) * 2 * (size_t)n_grid * p.n_t_tiles * p.n_o_tiles);
   p.off_s = off;
   off = align256(off + sizeof(float) * (size_t)n_grid * in_features);
   p.off_inv_s = off;
@@ -278,7 +278,7 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
   }
   if (stage_mask & 4) {  // select
     hipLaunchKernelGGL(k_argmin, dim3(1), dim3(kArgminThreads), 0, stream, partials,
-                       p.n_t_tiles * p.n_o_tiles, n_grid, (double)N * (double)OUT, s_tab, K,
+                       2 * p.n_t_tiles * p.n_o_tiles, n_grid, (double)N * (double)OUT, s_tab, K,
                        losses, best_idx, s_best);
   }
   return hipGetLastError();

@@ -42,10 +42,20 @@
 //   * Operand k mapping: lane l holds k0 + 8*(l/16) .. +7 of row (l % 16) for
 //     both A (tokens) and B (outputs), so each MFMA sums matching k pairs.
 //     Accumulator register r of lane l holds C[4*(l/16) + r][l % 16].
-//   * Block order: linear block b runs on XCD b % 8.  The j-th block an XCD
-//     receives takes grid point j % n_grid of tile 8*(j / n_grid) + xcd, so
-//     the blocks resident on one XCD at a time are the grid points of one or
-//     two tiles and share the tiles' activation and weight rows in that XCD's L2.
+//   * Block order: linear block b runs on XCD b % 8.  Work unit u (one grid
+//     point of one tile) is taken by the u-th block; the j-th unit an XCD
+//     receives is grid point j % n_grid of tile 8*(j / n_grid) + xcd, so the
+//     blocks resident on one XCD at a time are the grid points of one or two
+//     tiles and share the tiles' activation and weight rows in that XCD's L2.
+//   * Last round: when the units do not fill the chip a whole number of
+//     times and the leftover units fill at most half of it, the leftover
+//     units run as a second launch of the half-height kernel, two blocks per
+//     unit (the halves of the tile's tokens, on the unit's XCD), so the last
+//     round takes about half as long.  Each unit owns two partial-sum slots;
+//     a whole-tile block writes its sum and a zero, a half-tile block its half.
+#include <map>
+#include <mutex>
+
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -56,7 +66,7 @@ __global__ void __launch_bounds__(NW * 64, 1)
 k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
        const float* __restrict__ s_tab, const float* __restrict__ inv_tab,
        const GroupParams* __restrict__ prm, double* __restrict__ partials, int N, int K,
-       int OUT, int n_t_tiles, int n_o_tiles, int n_grid) {
+       int OUT, int n_t_tiles, int n_o_tiles, int n_grid, int unit_base, int split) {
   constexpr int NT = NW * 64;
   constexpr int KC = 32;            // k per step (one 16x16x32 MFMA deep)
   constexpr int WMT = BM / NW;      // tokens per wavefront
@@ -72,14 +82,22 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   __shared__ double red[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n_items = n_grid;
   const int n_tiles = n_t_tiles * n_o_tiles;
-  const int jb = blockIdx.x >> 3;
-  const int ai = jb % n_items;
-  const int T = (jb / n_items) * 8 + (blockIdx.x & 7);
+  // unit u and token half h: whole tiles take one block per unit; halves take
+  // blocks b and b + 8 (same XCD) for the two halves of unit base + b%8 + 8(b/16)
+  const int b = blockIdx.x;
+  const int u = unit_base + (split == 1 ? b : (b & 7) + 8 * (b >> 4));
+  const int h = split == 1 ? 0 : (b >> 3) & 1;
+  const int jb = u >> 3;
+  const int ai = jb % n_grid;
+  const int T = (jb / n_grid) * 8 + (u & 7);
   if (T >= n_tiles) return;
   const int tt = T / n_o_tiles, ot = T - tt * n_o_tiles;
-  const int t0 = tt * BM, o0 = ot * BN;
+  const int t0 = tt * BM * split + h * BM, o0 = ot * BN;
+  if (t0 >= N) {  // second half of a ragged last token tile: no rows
+    if (threadIdx.x == 0) partials[2 * ((size_t)ai * n_tiles + T) + h] = 0.0;
+    return;
+  }
   const int ngroups = K >> 7;
   const int nk = K / KC;  // a multiple of 4
   const float nz = neg_zero();
@@ -285,7 +303,13 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
     double tot = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot += red[w];
-    partials[(size_t)ai * n_tiles + T] = tot;
+    double* slot = partials + 2 * ((size_t)ai * n_tiles + T);
+    if (split == 1) {
+      slot[0] = tot;
+      slot[1] = 0.0;
+    } else {
+      slot[h] = tot;
+    }
   }
 }
 
@@ -302,32 +326,70 @@ int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
 }
 
 template <int BM, int NW>
-static void launch_one(dim3 grid, hipStream_t stream, const _Float16* X, const _Float16* W,
-                       const float* s_tab, const float* inv_tab, const GroupParams* prm,
-                       double* partials, int N, int K, int OUT, int nt, int no, int n_grid) {
-  hipLaunchKernelGGL((k_grid<BM, kGridBN, NW>), grid, dim3(NW * 64), 0, stream, X, W, s_tab,
-                     inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
+static void launch_one(unsigned blocks, int unit_base, int split, hipStream_t stream,
+                       const _Float16* X, const _Float16* W, const float* s_tab,
+                       const float* inv_tab, const GroupParams* prm, double* partials, int N,
+                       int K, int OUT, int nt, int no, int n_grid) {
+  hipLaunchKernelGGL((k_grid<BM, kGridBN, NW>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
+                     s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base, split);
+}
+
+// Blocks of the whole-tile kernel that run at once on the current device
+// (compute units x resident blocks per unit), cached per device and tile.
+template <int BM, int NW>
+static int64_t resident_blocks() {
+  static std::mutex mu;
+  static std::map<int, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid<BM, kGridBN, NW>, NW * 64, 0) !=
+          hipSuccess)
+    return 0;
+  const int64_t r = (int64_t)cus * per_cu;
+  cache[dev] = r;
+  return r;
+}
+
+template <int BM, int NW, int HBM, int HNW>
+static void launch_split(int64_t units, hipStream_t stream, const _Float16* X, const _Float16* W,
+                         const float* s_tab, const float* inv_tab, const GroupParams* prm,
+                         double* partials, int N, int K, int OUT, int nt, int no, int n_grid) {
+  const int64_t slots = resident_blocks<BM, NW>();
+  int64_t whole = units;
+  if (slots > 0) {
+    const int64_t rest = units % slots;
+    if (units > slots && rest > 0 && rest % 8 == 0 && 2 * rest <= slots) whole = units - rest;
+  }
+  launch_one<BM, NW>((unsigned)whole, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials, N, K,
+                     OUT, nt, no, n_grid);
+  if (whole < units)  // whole and units are multiples of 8
+    launch_one<HBM, HNW>((unsigned)(2 * (units - whole)), (int)whole, 2, stream, X, W, s_tab,
+                         inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
 }
 
 void launch_grid(int tile_m, const void* X, const void* W, const float* s_tab,
                  const float* inv_tab, const GroupParams* prm, double* partials, int64_t N,
                  int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream) {
-  const int64_t tiles8 = (nt * no + 7) / 8 * 8;
-  const dim3 grid((unsigned)(tiles8 * n_grid));
+  const int64_t units = (nt * no + 7) / 8 * 8 * n_grid;
   const _Float16* Xh = (const _Float16*)X;
   const _Float16* Wh = (const _Float16*)W;
   switch (tile_m) {
     case 512:
-      launch_one<512, 8>(grid, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
-                         (int)OUT, (int)nt, (int)no, n_grid);
+      launch_split<512, 8, 256, 8>(units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
+                                   (int)K, (int)OUT, (int)nt, (int)no, n_grid);
       break;
     case 256:
-      launch_one<256, 8>(grid, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
-                         (int)OUT, (int)nt, (int)no, n_grid);
+      launch_split<256, 8, 128, 4>(units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
+                                   (int)K, (int)OUT, (int)nt, (int)no, n_grid);
       break;
     default:
-      launch_one<128, 4>(grid, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
-                         (int)OUT, (int)nt, (int)no, n_grid);
+      launch_one<128, 4>((unsigned)units, 0, 1, stream, Xh, Wh, s_tab, inv_tab, prm, partials,
+                         (int)N, (int)K, (int)OUT, (int)nt, (int)no, n_grid);
       break;
   }
 }

@@ -114,7 +114,7 @@ def test_search_plan_layout(lib):
     assert plan.n_token_tiles == -(-1000 // plan.tile_tokens)
     assert plan.n_out_tiles == -(-1000 // plan.tile_out)
     regions = sorted([
-        (plan.partials_offset, 8 * 20 * plan.n_token_tiles * plan.n_out_tiles),
+        (plan.partials_offset, 16 * 20 * plan.n_token_tiles * plan.n_out_tiles),
         (plan.scales_offset, 4 * 20 * 4096)])
     for (a, la), (b, _) in zip(regions, regions[1:]):
         assert a + la <= b
@@ -123,7 +123,7 @@ def test_search_plan_layout(lib):
         assert off % 256 == 0
     # scale tables and per-group parameters dominate; there is no N x OUT buffer
     params = 16 * 20 * 1000 * (4096 // 128)
-    assert plan.workspace_bytes < params + 2 * 4 * 20 * 4096 + 8 * 20 * 64 + 4096
+    assert plan.workspace_bytes < params + 2 * 4 * 20 * 4096 + 16 * 20 * 64 + 4096
 
 
 def test_stats_validation(lib):

@@ -198,6 +198,22 @@ def test_search_edge_shapes(awq, n, k, o, n_grid):
     check_best(int(host(res.best_idx)[0]), ref.losses)
 
 
+@pytest.mark.parametrize("n,k,o", [(700, 256, 2048), (300, 256, 2048)])
+def test_search_split_last_round(awq, n, k, o):
+    """Shapes whose work units fill the chip 2.5 times: the last half round runs
+    as half-height tiles, and the second half of the ragged last token tile is
+    empty."""
+    _say(f"search split last round {n}x{k}->{o}")
+    _, X, W = synth.make_custom(n, k, o, seed=n + o)
+    Xd, Wd, sal, res = run_layer(awq, X, W)
+    ref = O.search_layer(X, W, host(sal))
+    losses = host(res.losses)
+    rel = np.abs(losses - ref.losses) / ref.losses
+    _say(f"  max rel loss diff {rel.max():.3e}")
+    assert np.all(rel <= LOSS_RTOL)
+    check_best(int(host(res.best_idx)[0]), ref.losses)
+
+
 def test_search_degenerate_inputs(awq):
     # all-zero activations: saliency 0 is floored, every loss is 0, the first wins
     X = np.zeros((16, 256), np.float16)
@@ -236,8 +252,8 @@ def test_full_size_layer_sampled_tiles(awq, cfg, layer):
     ws = res.workspace
     n_grid = 20
     nt, no = plan.n_token_tiles, plan.n_out_tiles
-    part = host(ws[plan.partials_offset:plan.partials_offset + 8 * n_grid * nt * no]
-                .view(torch.float64)).reshape(n_grid, nt, no)
+    part = host(ws[plan.partials_offset:plan.partials_offset + 16 * n_grid * nt * no]
+                .view(torch.float64)).reshape(n_grid, nt, no, 2).sum(axis=3)
     losses = host(res.losses)
     count = float(spec.n_tokens) * spec.out_features
     assert np.allclose(losses, part.reshape(n_grid, -1).sum(axis=1) / count, rtol=1e-12)
