@@ -88,6 +88,9 @@ const char* awq_version(void);
  *   X:        [n_tokens, in_features] fp16, read only
  *   sal_out:  [in_features] fp32, written
  *   n_tokens >= 1, in_features >= 8 and a multiple of 8.
+ * The workspace holds per-row-chunk partial column sums (64-bit integers):
+ * between 8 * in_features and 8 * in_features * (1 + n_tokens / 64) bytes.
+ * Its contents on entry do not matter.
  * Source: dev.to page, channel_importance listing; Summary page,
  * "Salient weight identification".
  * ---------------------------------------------------------------------- */

@@ -102,7 +102,7 @@ class SearchResult:
     losses: torch.Tensor     # [n_grid] float64 (device)
     best_idx: torch.Tensor   # [1] int32 (device); -1 when no loss is finite
     s_best: torch.Tensor     # [in] float32 (device)
-    workspace: torch.Tensor  # uint8 workspace (partials, X W^T, scale table, ...)
+    workspace: torch.Tensor  # uint8 workspace (tile partial sums, scale table, group parameters)
     plan: AwqSearchPlan
 
 

@@ -13,6 +13,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq_mi355x.so")
 SOURCES = ["act_stats.hip", "search.hip", "search_grid.hip", "pack.hip", "awq_api.hip"]
+# measured-peak references used by bench.py only (not part of the search library)
+CALIB_LIB = os.path.join(PKG, "libawq_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
@@ -62,6 +65,10 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    ctmp = CALIB_LIB + ".tmp"
+    _run([cc, *HIPCC_FLAGS, "-shared", "-o", ctmp,
+          *[os.path.join(CSRC, s) for s in CALIB_SOURCES]])
+    os.replace(ctmp, CALIB_LIB)
     if verbose:
         for o in outs:
             if o.strip():

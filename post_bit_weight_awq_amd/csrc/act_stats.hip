@@ -6,10 +6,12 @@
 // HBM-bound column reduction.  Each lane owns 8 consecutive columns and reads
 // them with one 16-byte load per token row, so a wavefront reads 1 KiB of a row
 // contiguously.  The block's four wavefronts take interleaved rows of one row
-// chunk.  |x| of an fp16 value is an integer multiple of 2^-24 below 2^16, so
-// the per-lane binary64 sums are exact (at most 8192 rows per chunk), and the
-// block total is added into a 64-bit integer accumulator in units of 2^-24:
-// the result is exact and independent of the order of the additions.
+// chunk, eight rows in flight per lane.  |x| of an fp16 value is an integer
+// multiple of 2^-24 below 2^16, so the per-lane binary64 sums are exact (at
+// most 8192 rows per chunk); the block's column totals are stored as 64-bit
+// integers in units of 2^-24, one row of partials per chunk.  A second kernel
+// adds each column's partials (integer adds: exact, in a fixed order) and
+// divides once.  Two launches, no atomics, no state kept between calls.
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -18,14 +20,9 @@ namespace awq {
 constexpr int kStatsThreads = 256;
 constexpr int kStatsCols = kWave * 8;  // columns per block
 
-__global__ void __launch_bounds__(256) k_fill_u64(unsigned long long* p, int64_t n) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0ull;
-}
-
 __global__ void __launch_bounds__(kStatsThreads)
 k_act_stats(const uint4* __restrict__ X, int64_t n_tokens, int64_t in_features,
-            int64_t rows_per_chunk, unsigned long long* __restrict__ acc) {
+            int64_t rows_per_chunk, unsigned long long* __restrict__ part) {
   __shared__ double red[kStatsThreads / kWave][kStatsCols];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -39,13 +36,13 @@ k_act_stats(const uint4* __restrict__ X, int64_t n_tokens, int64_t in_features,
   if (col < in_features) {
     const uint4* p = X + r0 * row_vecs + col / 8;
     int64_t r = r0 + wave;
-    // four rows in flight per lane
-    for (; r + 12 < r1; r += 16) {
-      uint4 v[4];
+    // eight rows in flight per lane
+    for (; r + 28 < r1; r += 32) {
+      uint4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = p[(r - r0 + 4 * u) * row_vecs];
+      for (int u = 0; u < 8; ++u) v[u] = p[(r - r0 + 4 * u) * row_vecs];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -69,24 +66,37 @@ k_act_stats(const uint4* __restrict__ X, int64_t n_tokens, int64_t in_features,
   __syncthreads();
   // 512 column totals, two per thread; the four wave partials are exact, so
   // their sum is exact as well.
+  unsigned long long* prow = part + (int64_t)blockIdx.y * in_features;
   for (int c = threadIdx.x; c < kStatsCols; c += kStatsThreads) {
     const int64_t gc = (int64_t)blockIdx.x * kStatsCols + c;
     if (gc < in_features) {
-      double t = red[0][c] + red[1][c] + red[2][c] + red[3][c];
-      unsigned long long u = (unsigned long long)(t * 16777216.0);  // exact: t is a multiple of 2^-24
-      if (u) atomicAdd(acc + gc, u);
+      const double t = red[0][c] + red[1][c] + red[2][c] + red[3][c];
+      prow[gc] = (unsigned long long)(t * 16777216.0);  // exact: t is a multiple of 2^-24
     }
   }
 }
 
-__global__ void __launch_bounds__(256)
-k_stats_finalize(const unsigned long long* __restrict__ acc, int64_t in_features,
-                 int64_t n_tokens, float* __restrict__ sal) {
-  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k < in_features) {
+// One block per 64 columns; its 16 wavefronts add every 16th chunk's partials
+// (lanes on consecutive columns), then wavefront 0 adds the 16 sums.  Integer
+// adds, so the total is exact whatever the order.
+__global__ void __launch_bounds__(1024)
+k_stats_finalize(const unsigned long long* __restrict__ part, int64_t row_chunks,
+                 int64_t in_features, int64_t n_tokens, float* __restrict__ sal) {
+  __shared__ unsigned long long sh[16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t k = (int64_t)blockIdx.x * 64 + lane;
+  unsigned long long acc = 0;
+  if (k < in_features)
+    for (int64_t c = wave; c < row_chunks; c += 16) acc += part[c * in_features + k];
+  sh[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && k < in_features) {
+    unsigned long long tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) tot += sh[w][lane];
     // binary64 value of the exact sum (rounded only beyond 2^53 units), then
     // the binary64 quotient, then binary32.
-    double total = (double)acc[k] * 0x1p-24;
+    const double total = (double)tot * 0x1p-24;
     sal[k] = (float)(total / (double)n_tokens);
   }
 }
@@ -94,31 +104,31 @@ k_stats_finalize(const unsigned long long* __restrict__ acc, int64_t in_features
 StatsPlan stats_plan(int64_t n_tokens, int64_t in_features) {
   StatsPlan p;
   p.col_blocks = (in_features + kStatsCols - 1) / kStatsCols;
-  // enough blocks to cover the chip several times over, chunks of >= 16 rows
-  int64_t want = (2048 + p.col_blocks - 1) / p.col_blocks;
-  int64_t max_chunks = (n_tokens + 15) / 16;
+  // about four blocks per compute unit, each streaming at least 64 rows (a
+  // multiple of 32: eight rows per wavefront per batch)
+  const int64_t want = (1024 + p.col_blocks - 1) / p.col_blocks;
+  const int64_t max_chunks = (n_tokens + 63) / 64;
   p.row_chunks = want < max_chunks ? want : max_chunks;
   if (p.row_chunks < 1) p.row_chunks = 1;
   p.rows_per_chunk = (n_tokens + p.row_chunks - 1) / p.row_chunks;
+  p.rows_per_chunk = (p.rows_per_chunk + 31) / 32 * 32;
   if (p.rows_per_chunk > 8192) {  // keep the per-lane binary64 sums exact
     p.rows_per_chunk = 8192;
   }
   p.row_chunks = (n_tokens + p.rows_per_chunk - 1) / p.rows_per_chunk;
-  p.workspace_bytes = (size_t)in_features * sizeof(unsigned long long);
+  p.workspace_bytes = (size_t)p.row_chunks * in_features * sizeof(unsigned long long);
   return p;
 }
 
 hipError_t launch_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal,
                             void* workspace, hipStream_t stream) {
   const StatsPlan p = stats_plan(n_tokens, in_features);
-  unsigned long long* acc = (unsigned long long*)workspace;
-  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)((in_features + 255) / 256)), dim3(256), 0, stream,
-                     acc, in_features);
+  unsigned long long* part = (unsigned long long*)workspace;
   hipLaunchKernelGGL(k_act_stats, dim3((unsigned)p.col_blocks, (unsigned)p.row_chunks),
                      dim3(kStatsThreads), 0, stream, (const uint4*)X, n_tokens, in_features,
-                     p.rows_per_chunk, acc);
-  hipLaunchKernelGGL(k_stats_finalize, dim3((unsigned)((in_features + 255) / 256)), dim3(256), 0,
-                     stream, acc, in_features, n_tokens, sal);
+                     p.rows_per_chunk, part);
+  hipLaunchKernelGGL(k_stats_finalize, dim3((unsigned)((in_features + 63) / 64)), dim3(1024), 0,
+                     stream, part, p.row_chunks, in_features, n_tokens, sal);
   return hipGetLastError();
 }
 

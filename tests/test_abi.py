@@ -154,3 +154,11 @@ def test_python_binding_rejects_cpu_tensors():
     X = torch.zeros(4, 128, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         awq.awq_act_stats(X, out=torch.empty(128), workspace=torch.empty(4096, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("n,k", [(1, 8), (63, 512), (64, 4096), (512, 4096), (4096, 13824),
+                                 (9000, 64), ((1 << 20) + 3, 1024)])
+def test_stats_workspace_bounds(lib, n, k):
+    need = lib.awq_act_stats_workspace_size(n, k)
+    assert need % 8 == 0
+    assert 8 * k <= need <= 8 * k * (1 + n // 64)
