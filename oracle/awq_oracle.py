@@ -1,4 +1,5 @@
-"""CPU oracle for the AWQ per-layer search path -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the AWQ per-layer search path and for inference with its
+packed output -- TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the package's smoke check and the benchmark's CPU
 baseline leg may import this module.  The product path never calls it: it is
@@ -314,3 +315,39 @@ def packed_bytes(n_weights: int, group: int = GROUP, w_bit: int = W_BIT) -> dict
         "zeros": n_weights // group * 2,
         "fp16": n_weights * 2,
     }
+
+
+# --------------------------------------------------------------------------
+# inference with the packed weights: W4A16 product y = x Wdq^T
+# --------------------------------------------------------------------------
+def dequant_packed(qweight: np.ndarray, step16: np.ndarray, zero16: np.ndarray,
+                   group: int = GROUP) -> np.ndarray:
+    """The real-valued weight the packed format stands for, (q - z) * step per
+    element, exact in binary64 (q a 4-bit code, z and step the stored fp16
+    values of the element's group): the inverse map of the step-size
+    equation of [P4], applied to the INT32-packed codes of [P2]."""
+    q = unpack_codes(qweight).astype(F64)
+    st = np.repeat(np.asarray(step16, F16).astype(F64), group, axis=1)
+    zr = np.repeat(np.asarray(zero16, F16).astype(F64), group, axis=1)
+    return (q - zr) * st
+
+
+def w4a16_matmul(x: np.ndarray, qweight: np.ndarray, step16: np.ndarray, zero16: np.ndarray,
+                 group: int = GROUP) -> np.ndarray:
+    """Decode-time product of fp16 activations with the packed 4-bit weights
+    (W4A16, [P1] "What do you actually deploy": 4-bit weights, 16-bit
+    activations, groups of 128 with a zero point; decode streams the packed
+    weights instead of fp16 ones): y[t, o] = sum_k x[t, k] (q[o, k] - z) step,
+    in binary64.  The activations are whatever the caller feeds the layer
+    (after the 1/s fold, x / s)."""
+    return np.asarray(x, F16).astype(F64) @ dequant_packed(qweight, step16, zero16, group).T
+
+
+def w4a16_abs_matmul(x: np.ndarray, qweight: np.ndarray, step16: np.ndarray,
+                     zero16: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """sum_k |x[t, k]| (|q| + |z|) |step|: the scale of the rounding-error
+    bound of any binary32 evaluation of w4a16_matmul (error bounds only)."""
+    q = unpack_codes(qweight).astype(F64)
+    st = np.abs(np.repeat(np.asarray(step16, F16).astype(F64), group, axis=1))
+    zr = np.abs(np.repeat(np.asarray(zero16, F16).astype(F64), group, axis=1))
+    return np.abs(np.asarray(x, F16).astype(F64)) @ ((q + zr) * st).T

@@ -369,6 +369,49 @@ def test_pack_layout_and_roundtrip():
     assert np.array_equal(O.unpack_codes(O.pack_codes(qq)), qq)
 
 
+# ------------------------------------------------- W4A16 product (decode)
+def _random_packed(rng, rows, k):
+    words = rng.integers(0, 2 ** 32, (rows, k // 8), dtype=np.uint64).astype(np.uint32)
+    step = rng.uniform(1e-3, 0.1, (rows, k // 128)).astype(F16)
+    zero = rng.integers(0, 16, (rows, k // 128)).astype(F16)
+    return words.view(np.int32), step, zero
+
+
+def test_w4a16_matches_exact_rationals():
+    """The W4A16 product against exact rational arithmetic on tiny inputs,
+    with the nibbles read from each 32-bit word by plain integer shifts
+    (column 8w + j in bits 4j..4j+3)."""
+    rng = np.random.default_rng(11)
+    rows, k, m = 3, 256, 2
+    qw, st, zr = _random_packed(rng, rows, k)
+    x = rng.standard_normal((m, k)).astype(F16)
+    y = O.w4a16_matmul(x, qw, st, zr)
+    for t in range(m):
+        for o in range(rows):
+            acc = Fraction(0)
+            for col in range(k):
+                word = int(qw.view(np.uint32)[o, col // 8])
+                code = (word >> (4 * (col % 8))) & 0xF
+                g = col // 128
+                acc += Fraction(float(x[t, col])) * (code - Fraction(float(zr[o, g]))) \
+                    * Fraction(float(st[o, g]))
+            assert y[t, o] == pytest.approx(float(acc), rel=1e-12, abs=1e-300)
+
+
+def test_w4a16_on_grid_weights_reproduce_the_layer():
+    """Weights on their group's grid (power-of-two steps) survive pack and the
+    W4A16 dequantization exactly, so the product equals x W^T."""
+    rng = np.random.default_rng(12)
+    k = 384
+    W, _ = _grid_layer(5, k, rng, np.ones(k))
+    p = O.pack(W, np.ones(k, F32))
+    assert np.array_equal(O.dequant_packed(p.qweight, p.step16, p.zero16), W.astype(F64))
+    x = rng.standard_normal((4, k)).astype(F16)
+    want = x.astype(F64) @ W.astype(F64).T
+    assert np.allclose(O.w4a16_matmul(x, p.qweight, p.step16, p.zero16), want, rtol=1e-14,
+                       atol=1e-14)
+
+
 def test_literal_division_changes_loss_negligibly():
     """Folding s back by multiplying with fp32(1/s) instead of dividing by s
     moves the dequantized weight by at most one fp16 rounding step."""
@@ -384,7 +427,7 @@ def test_literal_division_changes_loss_negligibly():
 
 # ------------------------------------------- planted mistakes must be caught
 @pytest.mark.parametrize("mutation", ["floor_round", "symmetric_step", "grid_to_one",
-                                      "no_zero_canon"])
+                                      "no_zero_canon", "nibble_order"])
 def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
     """Each plausible slip in the oracle trips at least one pin above."""
     if mutation == "floor_round":
@@ -406,6 +449,16 @@ def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
         monkeypatch.setattr(O, "alphas", lambda n=20: np.arange(n, dtype=F64) / (n - 1))
         with pytest.raises(AssertionError):
             test_single_outlier_loss_closed_form_and_monotone()
+    elif mutation == "nibble_order":
+        orig = O.unpack_codes
+
+        def reversed_nibbles(qweight):
+            u = orig(qweight)
+            r, k = u.shape
+            return u.reshape(r, k // 8, 8)[:, :, ::-1].reshape(r, k)
+        monkeypatch.setattr(O, "unpack_codes", reversed_nibbles)
+        with pytest.raises(AssertionError):
+            test_w4a16_matches_exact_rationals()
     elif mutation == "no_zero_canon":
         orig = O.quantize
 
