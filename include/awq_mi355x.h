@@ -173,6 +173,32 @@ int awq_pack(const void* W, const float* s, int64_t in_features, int64_t out_fea
              const awq_config* cfg, int32_t* qweight_out, void* step_out, void* zero_out,
              void* stream);
 
+/* ------------------------------------------------------------------------
+ * Inference with the packed weights (W4A16): for every token t and output o
+ *   Y[t, o] = sum_k X[t, k] * (q[o, k] - zero[o, k/128]) * step[o, k/128]
+ * with q the 4-bit codes of awq_pack's qweight (nibble j of word w = column
+ * 8w + j) and step/zero its fp16 group values.  The activations are what the
+ * layer receives after the 1/s fold (x / s); fp16 products are exact and are
+ * accumulated in binary32, the group's step and zero applied once per group
+ * as step * (sum x q - zero * sum x).
+ *   X:       [n_tokens, in_features] fp16, read only, 16-byte aligned
+ *   qweight: [out_features, in_features/8] int32, 16-byte aligned
+ *   step16, zero16: [out_features, in_features/128] fp16, 2-byte aligned
+ *   Y:       [n_tokens, out_features] fp32, written, 4-byte aligned
+ *   in_features a positive multiple of 128; 1 <= n_tokens <= 1048560.
+ * Built for decode: one block per 16 output rows and 16 tokens, so the
+ * weights stream from HBM once when n_tokens <= 16 (HBM-bound at 0.53 byte
+ * per weight); larger n_tokens re-read them once per 16 tokens.
+ * Errors: AWQ_ERR_INVALID_ARG for NULL or misaligned pointers and sizes out
+ * of range (nothing is enqueued); AWQ_ERR_HIP for a launch failure.
+ * Source: dev.to page, "What do you actually deploy" (4-bit weights, 16-bit
+ * activations, group size 128; decode moves a quarter of the weight bytes);
+ * esaholic.com page, INT4 in INT32 containers and W4A16 GEMM kernels.
+ * ---------------------------------------------------------------------- */
+int awq_w4a16_matmul(const void* X, int64_t n_tokens, int64_t in_features, int64_t out_features,
+                     const int32_t* qweight, const void* step16, const void* zero16, float* Y,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ from ._lib import STAGE_ALL, STAGE_GRID, STAGE_PREPARE, STAGE_SELECT  # noqa: F4
 
 __all__ = ["AwqConfig", "AwqError", "default_config", "awq_act_stats",
            "awq_act_stats_workspace_size", "awq_search_plan", "awq_search_workspace_size",
-           "awq_search_layer", "awq_pack", "SearchResult", "load"]
+           "awq_search_layer", "awq_pack", "awq_w4a16_matmul", "SearchResult", "load"]
 
 
 def default_config(n_grid: int = 20, sal_floor: float = 1e-4) -> AwqConfig:
@@ -171,3 +171,25 @@ def awq_pack(W: torch.Tensor, s: torch.Tensor, cfg: Optional[AwqConfig] = None, 
         ctypes.c_void_p(_dev(zero, "zero", torch.float16, (o, k // g))),
         _stream(stream)))
     return qweight, step, zero
+
+
+def awq_w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, step: torch.Tensor,
+                     zero: torch.Tensor, *, out: Optional[torch.Tensor] = None, stream=None):
+    """Y [n_tokens, out_features] fp32 = X (q - zero) step, with (qweight, step,
+    zero) as awq_pack returns them and X [n_tokens, in_features] fp16."""
+    if X.dim() != 2 or qweight.dim() != 2:
+        raise ValueError("X must be [n_tokens, in_features], qweight [out_features, in_features/8]")
+    n, k = X.shape
+    o = qweight.shape[0]
+    if k % 128:
+        raise ValueError(f"in_features={k} must be a multiple of 128")
+    if out is None:
+        out = torch.empty((n, o), dtype=torch.float32, device=X.device)
+    check(load().awq_w4a16_matmul(
+        ctypes.c_void_p(_dev(X, "X", torch.float16, (n, k))), n, k, o,
+        ctypes.c_void_p(_dev(qweight, "qweight", torch.int32, (o, k // 8))),
+        ctypes.c_void_p(_dev(step, "step", torch.float16, (o, k // 128))),
+        ctypes.c_void_p(_dev(zero, "zero", torch.float16, (o, k // 128))),
+        ctypes.c_void_p(_dev(out, "out", torch.float32, (n, o))),
+        _stream(stream)))
+    return out

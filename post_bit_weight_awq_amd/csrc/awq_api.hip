@@ -193,4 +193,21 @@ int awq_pack(const void* W, const float* s, int64_t in_features, int64_t out_fea
                     "awq_pack launch");
 }
 
+int awq_w4a16_matmul(const void* X, int64_t n_tokens, int64_t in_features, int64_t out_features,
+                     const int32_t* qweight, const void* step16, const void* zero16, float* Y,
+                     void* stream) {
+  int rc;
+  if ((rc = check_dims(1, in_features, out_features, false, true, 128))) return rc;
+  if (n_tokens < 1 || n_tokens > awq::kMaxW4Tokens)
+    return fail(AWQ_ERR_INVALID_ARG, "n_tokens=%lld outside 1..%lld", (long long)n_tokens,
+                (long long)awq::kMaxW4Tokens);
+  if ((rc = check_ptr(X, "X")) || (rc = check_ptr(qweight, "qweight"))) return rc;
+  if (!step16 || !zero16 || !Y) return fail(AWQ_ERR_INVALID_ARG, "step16/zero16/Y is NULL");
+  if (((uintptr_t)step16 & 1u) || ((uintptr_t)zero16 & 1u) || ((uintptr_t)Y & 3u))
+    return fail(AWQ_ERR_INVALID_ARG, "step16/zero16 must be 2-byte and Y 4-byte aligned");
+  return hip_result(awq::launch_w4a16(X, n_tokens, in_features, out_features, qweight, step16,
+                                      zero16, Y, (hipStream_t)stream),
+                    "awq_w4a16_matmul launch");
+}
+
 }  // extern "C"

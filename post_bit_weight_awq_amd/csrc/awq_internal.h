@@ -41,6 +41,11 @@ void launch_grid(int tile_m, const void* X, const void* W, const float* s_tab,
 // largest grid the grid kernel is launched with (blocks of 256 threads in x)
 constexpr int64_t kMaxGridBlocks = (int64_t)1 << 23;
 
+hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const int32_t* qweight,
+                        const void* step16, const void* zero16, float* Y, hipStream_t stream);
+// largest token count of one W4A16 launch (16 tokens per block row of the grid)
+constexpr int64_t kMaxW4Tokens = (int64_t)65535 * 16;
+
 hipError_t launch_pack(const void* W, const float* s, int64_t in_features, int64_t out_features,
                        int32_t* qweight, void* step16, void* zero16, hipStream_t stream);
 

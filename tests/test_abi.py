@@ -162,3 +162,21 @@ def test_stats_workspace_bounds(lib, n, k):
     need = lib.awq_act_stats_workspace_size(n, k)
     assert need % 8 == 0
     assert 8 * k <= need <= 8 * k * (1 + n // 64)
+
+
+def test_w4a16_validation(lib):
+    args = [FAKE, 4, 256, 32, FAKE, FAKE, FAKE, FAKE, None]
+    for pos, bad in ((1, 0), (1, (1 << 20) + 1), (2, 200), (2, 0), (3, 0)):
+        a = list(args)
+        a[pos] = bad
+        assert lib.awq_w4a16_matmul(*a) == _lib.AWQ_ERR_INVALID_ARG, (pos, bad)
+    for pos in (0, 4, 5, 6, 7):
+        a = list(args)
+        a[pos] = None
+        assert lib.awq_w4a16_matmul(*a) == _lib.AWQ_ERR_INVALID_ARG, pos
+    for pos, ptr in ((0, MISALIGNED), (4, MISALIGNED), (5, ctypes.c_void_p(0x1001)),
+                     (7, ctypes.c_void_p(0x1002))):
+        a = list(args)
+        a[pos] = ptr
+        assert lib.awq_w4a16_matmul(*a) == _lib.AWQ_ERR_INVALID_ARG, pos
+        assert lib.awq_last_error()

@@ -274,3 +274,54 @@ def test_full_size_layer_sampled_tiles(awq, cfg, layer):
             worst = max(worst, abs(got - want) / want)
             assert abs(got - want) <= LOSS_RTOL * want, (ti, oi, i, got, want)
     _say(f"  worst sampled tile rel diff {worst:.3e}, best {best}")
+
+
+# ------------------------------------------- W4A16 product with packed weights
+def _w4a16_check(awq, x, qw, st, zr):
+    y = host(awq.awq_w4a16_matmul(dev(x), dev(qw), dev(st), dev(zr)))
+    want = O.w4a16_matmul(x, qw, st, zr)
+    scale = O.w4a16_abs_matmul(x, qw, st, zr)
+    k = x.shape[1]
+    # binary32 accumulation of exact fp16 products: per group (<= 128 terms),
+    # two roundings for step * (sum x q - z sum x), then the groups and the
+    # 16 per-wavefront partials; bound with margin for the MFMA's summation order
+    tol = (k / 128 + 160) * 2.0 ** -22 * scale
+    err = np.abs(y.astype(np.float64) - want)
+    assert np.all(err <= tol + 1e-30), float((err / np.maximum(scale, 1e-30)).max())
+    return y, want
+
+
+W4_CASES = [(1, 4096, 4096), (3, 384, 17), (16, 128, 16), (17, 256, 33), (40, 5120, 300),
+            (1, 13824, 64), (2, 128, 1)]
+
+
+@pytest.mark.parametrize("m,k,o", W4_CASES)
+def test_w4a16_matches_oracle(awq, m, k, o):
+    _say(f"w4a16 {m}x{k} -> {o}")
+    _, X, W = synth.make_custom(max(m, 4), k, o, seed=m + k + o)
+    x = X[:m].copy()
+    sal = O.act_stats(X)
+    s, _ = O.scale_table(sal)
+    p = O.pack(W, s[9])
+    _w4a16_check(awq, x, p.qweight, p.step16, p.zero16)
+
+
+def test_w4a16_any_codes_and_zero_points(awq):
+    """Random codes and zero points far outside 0..15 (all-positive or
+    all-negative groups store such zeros): the zero enters once per group."""
+    rng = np.random.default_rng(21)
+    o, k, m = 48, 640, 5
+    qw = rng.integers(0, 2 ** 32, (o, k // 8), dtype=np.uint64).astype(np.uint32).view(np.int32)
+    st = rng.uniform(1e-4, 0.05, (o, k // 128)).astype(np.float16)
+    zr = rng.choice([-2000.0, -37.0, 0.0, 7.0, 15.0, 300.0, 4096.0], (o, k // 128)).astype(np.float16)
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    _w4a16_check(awq, x, qw, st, zr)
+
+
+def test_w4a16_after_gpu_pack(awq):
+    """The decode product consumes awq_pack's own output (search -> pack -> use)."""
+    _, X, W = synth.make_layer(3, n_tokens=64, out_features=256)
+    Xd, Wd, sal, res = run_layer(awq, X, W)
+    qw, st, zr = awq.awq_pack(Wd, res.s_best)
+    x = (X[:2].astype(np.float32) / host(res.s_best)[None, :]).astype(np.float16)
+    _w4a16_check(awq, x, host(qw), host(st), host(zr))
