@@ -191,6 +191,83 @@ def cold_measurements(awq, cfg, layers, calib):
     return res, round(mfma, 1)
 
 
+DECODE_LAYERS = (("qkv", 5120, 15360), ("o_proj", 5120, 5120), ("gate_up", 5120, 27648),
+                 ("down", 13824, 5120))
+
+
+def decode_bench(tokens, reps):
+    """W4A16 decode on the 13B block's four linears (packed by awq_pack from the
+    seeded synthetic weights): each measurement clears the 256 MB MALL with a
+    512 MiB read first, as a decode step over a whole model would find it."""
+    import numpy as np
+    import torch
+    import synth
+    import post_bit_weight_awq_amd as awq
+    calib = load_calib()
+    if calib is None:
+        raise RuntimeError("libawq_calib.so is missing: run post_bit_weight_awq_amd/build.py")
+    awq.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    layers = []
+    for li, (name, k, o) in enumerate(DECODE_LAYERS):
+        _, X, W = synth.make_custom(max(tokens), k, o, seed=1000 + li)
+        Wd = torch.from_numpy(W).cuda()
+        s = torch.ones(k, dtype=torch.float32, device="cuda")
+        qw, st, zr = awq.awq_pack(Wd, s)
+        del Wd
+        layers.append(dict(name=name, k=k, o=o, X=torch.from_numpy(X).cuda(), qw=qw, st=st, zr=zr))
+    torch.cuda.synchronize()
+    flush = torch.zeros(1 << 29, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def do_flush():
+        assert calib.awq_calib_read(flush.data_ptr(), flush.numel(), sink.data_ptr(), 2048,
+                                    stream) == 0
+
+    def median_ms(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            do_flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    def layer_bytes(L, m):
+        return (L["o"] * L["k"] // 2 + 4 * L["o"] * L["k"] // 128 + 2 * m * L["k"]
+                + 4 * m * L["o"])
+
+    res = {}
+    for m in tokens:
+        ys = [torch.empty((m, L["o"]), dtype=torch.float32, device="cuda") for L in layers]
+        xs = [L["X"][:m].contiguous() for L in layers]
+        per = {}
+        for L, x, y in zip(layers, xs, ys):
+            ms = median_ms(lambda: awq.awq_w4a16_matmul(x, L["qw"], L["st"], L["zr"], out=y))
+            rd = median_ms(lambda: calib.awq_calib_read(L["qw"].data_ptr(), L["qw"].numel() * 4,
+                                                        sink.data_ptr(), 4096, stream))
+            per[L["name"]] = {"shape": [m, L["k"], L["o"]], "us": round(ms * 1e3, 2),
+                              "gbs": round(layer_bytes(L, m) / (ms * 1e-3) / 1e9, 1),
+                              "plain_read_of_codes_gbs": round(L["qw"].numel() * 4 /
+                                                               (rd * 1e-3) / 1e9, 1)}
+
+        def block():
+            for L, x, y in zip(layers, xs, ys):
+                awq.awq_w4a16_matmul(x, L["qw"], L["st"], L["zr"], out=y)
+        ms = median_ms(block)
+        tot = sum(layer_bytes(L, m) for L in layers)
+        res[m] = {"block_us": round(ms * 1e3, 2), "block_gbs": round(tot / (ms * 1e-3) / 1e9, 1),
+                  "block_bytes": tot, "layers": per,
+                  "fp16_weights_us_at_same_rate": round(
+                      sum(2 * L["o"] * L["k"] for L in layers) / (tot / (ms * 1e-3)) * 1e6, 2)}
+    return res
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of a known size (PMC byte-counter scale)."""
     import torch
@@ -214,6 +291,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--decode", action="store_true",
+                    help="time the W4A16 product on packed weights (13B block, 1 and 16 tokens)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -224,6 +303,28 @@ def main():
 
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+
+    if args.decode:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        res = decode_bench((1, 16), max(5, args.steps))
+        one = res[1]
+        print(json.dumps({
+            "metric": "W4A16 decode product on packed AWQ weights, HBM GB/s (1 GPU)",
+            "value": one["block_gbs"], "unit": "GB/s", "n_gpus": 1, "steps": max(5, args.steps),
+            "warmup": 1, "ms_per_step": round(one["block_us"] / 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+            "data": "synthetic (seeded N(0,0.02) weights packed by awq_pack; N(0,1) activations)",
+            "config": {"workload": "llama13b_block_decode_w4a16_tok1",
+                       "layers": [list(x) for x in DECODE_LAYERS], "tokens": 1,
+                       "cache": "MALL cleared before each measurement"},
+            "roofline": {"bound": "hbm", "kernel": "k_w4a16", "achieved": one["block_gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(one["block_gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
+            "by_tokens": res}))
         return
 
     import numpy as np
