@@ -351,3 +351,23 @@ def w4a16_abs_matmul(x: np.ndarray, qweight: np.ndarray, step16: np.ndarray,
     st = np.abs(np.repeat(np.asarray(step16, F16).astype(F64), group, axis=1))
     zr = np.abs(np.repeat(np.asarray(zero16, F16).astype(F64), group, axis=1))
     return np.abs(np.asarray(x, F16).astype(F64)) @ ((q + zr) * st).T
+
+
+# --------------------------------------------------------------------------
+# folding 1/s into the operation that feeds the layer
+# --------------------------------------------------------------------------
+def fold_inverse_scale(src16: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Row j of src divided by s_j: dst = fp16(fp32(src) / s) row-wise.
+
+    The inverse of the per-channel scale is absorbed by whatever produces the
+    layer's input channels ([P4] "Salient Weight Preservation": the preceding
+    normalization's per-channel scale times 1/s_j; [P5] "Per-channel scaling":
+    the inverse is fused into preceding layers).  Rows are the layer's input
+    channels: a norm's gain or bias is a [n] (or [n, 1]) array, a preceding
+    linear's weight is [n, cols] and its bias [n].  The quotient is a binary32
+    division, rounded to fp16 (overflow gives an infinity)."""
+    a = np.asarray(src16, F16)
+    s = np.asarray(s, F32)
+    col = s.reshape((-1,) + (1,) * (a.ndim - 1))
+    with np.errstate(over="ignore"):
+        return (a.astype(F32) / col).astype(F32).astype(F16)

@@ -412,6 +412,66 @@ def test_w4a16_on_grid_weights_reproduce_the_layer():
                        atol=1e-14)
 
 
+# ------------------------------------------- folding 1/s into the producer
+def _rmsnorm64(h, gamma):
+    h = h.astype(F64)
+    return h / np.sqrt(np.mean(h * h, axis=1, keepdims=True) + 1e-6) * gamma.astype(F64)
+
+
+def test_fold_matches_exact_rationals():
+    rng = np.random.default_rng(31)
+    src = (rng.standard_normal((40, 3)) * rng.choice([1e-4, 1.0, 300.0], (40, 1))).astype(F16)
+    s = rng.uniform(0.05, 40.0, 40).astype(F32)
+    got = O.fold_inverse_scale(src, s)
+    for j in range(40):
+        for c in range(3):
+            q = Fraction(float(src[j, c])) / Fraction(float(s[j]))
+            want = brute.round_rne(brute.round_rne(q, brute.BINARY32), brute.BINARY16)
+            assert Fraction(float(got[j, c])) == want
+    big = O.fold_inverse_scale(np.array([60000.0, -60000.0], F16), np.array([0.5, 0.5], F32))
+    assert np.isposinf(big[0]) and np.isneginf(big[1])
+
+
+def test_fold_into_rmsnorm_preserves_the_layer():
+    """Salient Weight Preservation page: the norm's gain times 1/s cancels the
+    column scaling of W, so the scaled pair computes the same outputs; with
+    power-of-two s nothing rounds and the outputs agree exactly."""
+    rng = np.random.default_rng(32)
+    n, out = 256, 24
+    h = rng.standard_normal((6, n)).astype(F16)
+    gamma = rng.uniform(0.5, 1.5, n).astype(F16)
+    W = (rng.standard_normal((out, n)) * 0.05).astype(F16)
+    y = _rmsnorm64(h, gamma) @ W.astype(F64).T
+    s2 = (2.0 ** rng.integers(-3, 4, n)).astype(F32)
+    g2 = O.fold_inverse_scale(gamma, s2)
+    y2 = _rmsnorm64(h, g2) @ (W.astype(F64) * s2.astype(F64)[None, :]).T
+    assert np.array_equal(y2, y) or np.allclose(y2, y, rtol=1e-15, atol=0)
+    s = rng.uniform(0.1, 30.0, n).astype(F32)
+    g = O.fold_inverse_scale(gamma, s)
+    yf = _rmsnorm64(h, g) @ (W.astype(F64) * s.astype(F64)[None, :]).T
+    bound = (np.abs(_rmsnorm64(h, gamma)) @ np.abs(W.astype(F64)).T) * (2.0 ** -11 + 2.0 ** -23)
+    assert np.all(np.abs(yf - y) <= bound)
+
+
+def test_fold_into_previous_linear_preserves_the_layer():
+    """A preceding linear (weight rows and bias) absorbs 1/s the same way."""
+    rng = np.random.default_rng(33)
+    n, k, out = 128, 64, 16
+    h = rng.standard_normal((5, k)).astype(F16)
+    Wp = (rng.standard_normal((n, k)) * 0.1).astype(F16)
+    bp = rng.standard_normal(n).astype(F16)
+    W = (rng.standard_normal((out, n)) * 0.05).astype(F16)
+    s = rng.uniform(0.1, 30.0, n).astype(F32)
+    z = h.astype(F64) @ Wp.astype(F64).T + bp.astype(F64)
+    y = z @ W.astype(F64).T
+    zf = h.astype(F64) @ O.fold_inverse_scale(Wp, s).astype(F64).T \
+        + O.fold_inverse_scale(bp, s).astype(F64)
+    yf = zf @ (W.astype(F64) * s.astype(F64)[None, :]).T
+    zabs = np.abs(h.astype(F64)) @ np.abs(Wp.astype(F64)).T + np.abs(bp.astype(F64))
+    bound = (zabs @ np.abs(W.astype(F64)).T) * (2.0 ** -11 + 2.0 ** -23)
+    assert np.all(np.abs(yf - y) <= bound)
+
+
 def test_literal_division_changes_loss_negligibly():
     """Folding s back by multiplying with fp32(1/s) instead of dividing by s
     moves the dequantized weight by at most one fp16 rounding step."""
@@ -427,7 +487,7 @@ def test_literal_division_changes_loss_negligibly():
 
 # ------------------------------------------- planted mistakes must be caught
 @pytest.mark.parametrize("mutation", ["floor_round", "symmetric_step", "grid_to_one",
-                                      "no_zero_canon", "nibble_order"])
+                                      "no_zero_canon", "nibble_order", "fold_multiplies"])
 def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
     """Each plausible slip in the oracle trips at least one pin above."""
     if mutation == "floor_round":
@@ -459,6 +519,13 @@ def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
         monkeypatch.setattr(O, "unpack_codes", reversed_nibbles)
         with pytest.raises(AssertionError):
             test_w4a16_matches_exact_rationals()
+    elif mutation == "fold_multiplies":
+        monkeypatch.setattr(O, "fold_inverse_scale",
+                            lambda src, s: (np.asarray(src, F16).astype(F32)
+                                            * np.asarray(s, F32).reshape((-1,) + (1,) * (np.asarray(src).ndim - 1))
+                                            ).astype(F16))
+        with pytest.raises(AssertionError):
+            test_fold_into_rmsnorm_preserves_the_layer()
     elif mutation == "no_zero_canon":
         orig = O.quantize
 
