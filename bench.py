@@ -242,7 +242,25 @@ def decode_bench(tokens, reps):
         return (L["o"] * L["k"] // 2 + 4 * L["o"] * L["k"] // 128 + 2 * m * L["k"]
                 + 4 * m * L["o"])
 
-    res = {}
+    # folding s of the four searches upstream: the two norm gains, v_proj's rows
+    # (feeding o_proj) and up_proj's rows (feeding down), in place
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    fold_arrays = [("input_norm_gain", (5120,)), ("v_proj_weight", (5120, 5120)),
+                   ("post_attention_norm_gain", (5120,)), ("up_proj_weight", (13824, 5120))]
+    folds = []
+    for name, shape in fold_arrays:
+        a = torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.float16)
+        sv = torch.rand(shape[0], generator=gen, device="cuda") * 4 + 0.5
+        folds.append((name, a, sv))
+
+    def fold_all():
+        for _, a, sv in folds:
+            awq.awq_fold_inverse_scale(a, sv, out=a)
+    fold_ms = median_ms(fold_all)
+    fold_bytes = sum(4 * a.numel() + 4 * sv.numel() for _, a, sv in folds)
+    res = {"fold": {"arrays": [[n, list(a.shape)] for n, a, _ in folds],
+                    "us": round(fold_ms * 1e3, 2),
+                    "gbs": round(fold_bytes / (fold_ms * 1e-3) / 1e9, 1)}}
     for m in tokens:
         ys = [torch.empty((m, L["o"]), dtype=torch.float32, device="cuda") for L in layers]
         xs = [L["X"][:m].contiguous() for L in layers]
@@ -311,6 +329,7 @@ def main():
             print("bench.py: no GPU visible", file=sys.stderr)
             sys.exit(1)
         res = decode_bench((1, 16), max(5, args.steps))
+        fold = res.pop("fold")
         one = res[1]
         print(json.dumps({
             "metric": "W4A16 decode product on packed AWQ weights, HBM GB/s (1 GPU)",
@@ -324,7 +343,9 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "k_w4a16", "achieved": one["block_gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(one["block_gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
-            "by_tokens": res}))
+            "by_tokens": res,
+            "fold_inverse_scale": dict(fold, bound="hbm", peak_gbs=HBM_PEAK_GBS,
+                                       frac=round(fold["gbs"] / HBM_PEAK_GBS, 4))}))
         return
 
     import numpy as np

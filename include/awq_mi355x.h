@@ -199,6 +199,26 @@ int awq_w4a16_matmul(const void* X, int64_t n_tokens, int64_t in_features, int64
                      const int32_t* qweight, const void* step16, const void* zero16, float* Y,
                      void* stream);
 
+/* ------------------------------------------------------------------------
+ * Folding 1/s into whatever produces the layer's input channels:
+ *   dst[j, c] = fp16( fp32(src[j, c]) / s[j] )   (IEEE binary32 division)
+ * for a [rows, cols] fp16 array whose row j feeds input channel j: a norm's
+ * gain or bias (cols = 1), or a preceding linear's weight ([rows = its
+ * out_features, cols = its in_features]) and bias (cols = 1).  Overflow gives
+ * an infinity, as the division and rounding do.
+ *   src, dst: fp16, 2-byte aligned; dst may be src (in place) but must not
+ *             otherwise overlap it
+ *   s:        [rows] fp32 (the chosen s_best), 4-byte aligned
+ * Errors: AWQ_ERR_INVALID_ARG for NULL, misaligned or overlapping pointers
+ * and sizes out of range (nothing is enqueued); AWQ_ERR_HIP for a launch
+ * failure.
+ * Source: mbrenndoerfer.com "AWQ > Salient Weight Preservation" (the
+ * preceding normalization's per-channel scale absorbs 1/s_j); "AWQ > Summary",
+ * "Per-channel scaling" (the inverse is fused into preceding layers).
+ * ---------------------------------------------------------------------- */
+int awq_fold_inverse_scale(const void* src, const float* s, int64_t rows, int64_t cols, void* dst,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

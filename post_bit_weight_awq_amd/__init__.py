@@ -24,7 +24,7 @@ from ._lib import STAGE_ALL, STAGE_GRID, STAGE_PREPARE, STAGE_SELECT  # noqa: F4
 
 __all__ = ["AwqConfig", "AwqError", "default_config", "awq_act_stats",
            "awq_act_stats_workspace_size", "awq_search_plan", "awq_search_workspace_size",
-           "awq_search_layer", "awq_pack", "awq_w4a16_matmul", "SearchResult", "load"]
+           "awq_search_layer", "awq_pack", "awq_w4a16_matmul", "awq_fold_inverse_scale", "SearchResult", "load"]
 
 
 def default_config(n_grid: int = 20, sal_floor: float = 1e-4) -> AwqConfig:
@@ -191,5 +191,24 @@ def awq_w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, step: torch.Tensor,
         ctypes.c_void_p(_dev(step, "step", torch.float16, (o, k // 128))),
         ctypes.c_void_p(_dev(zero, "zero", torch.float16, (o, k // 128))),
         ctypes.c_void_p(_dev(out, "out", torch.float32, (n, o))),
+        _stream(stream)))
+    return out
+
+
+def awq_fold_inverse_scale(src: torch.Tensor, s: torch.Tensor, *,
+                           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Row j of the fp16 array src ([n] or [n, cols]) divided by s[j], in fp16:
+    the gain or bias of the norm, or the weight or bias of the linear, that
+    feeds the layer whose columns were scaled by s."""
+    if src.dim() not in (1, 2):
+        raise ValueError("src must be [n] or [n, cols]")
+    rows = src.shape[0]
+    cols = 1 if src.dim() == 1 else src.shape[1]
+    if out is None:
+        out = torch.empty_like(src)
+    check(load().awq_fold_inverse_scale(
+        ctypes.c_void_p(_dev(src, "src", torch.float16, tuple(src.shape))),
+        ctypes.c_void_p(_dev(s, "s", torch.float32, (rows,))), rows, cols,
+        ctypes.c_void_p(_dev(out, "out", torch.float16, tuple(src.shape))),
         _stream(stream)))
     return out

@@ -210,4 +210,21 @@ int awq_w4a16_matmul(const void* X, int64_t n_tokens, int64_t in_features, int64
                     "awq_w4a16_matmul launch");
 }
 
+int awq_fold_inverse_scale(const void* src, const float* s, int64_t rows, int64_t cols, void* dst,
+                           void* stream) {
+  if (!src || !s || !dst) return fail(AWQ_ERR_INVALID_ARG, "src/s/dst is NULL");
+  if (rows < 1 || rows > kMaxFeatures || cols < 1 || cols > kMaxFeatures || rows * cols > kMaxWeights)
+    return fail(AWQ_ERR_INVALID_ARG, "rows=%lld cols=%lld out of range", (long long)rows,
+                (long long)cols);
+  if (((uintptr_t)src & 1u) || ((uintptr_t)dst & 1u) || ((uintptr_t)s & 3u))
+    return fail(AWQ_ERR_INVALID_ARG, "src/dst must be 2-byte and s 4-byte aligned");
+  const char* a = (const char*)src;
+  const char* b = (const char*)dst;
+  const int64_t bytes = rows * cols * 2;
+  if (a != b && a < b + bytes && b < a + bytes)
+    return fail(AWQ_ERR_INVALID_ARG, "src and dst overlap without being the same array");
+  return hip_result(awq::launch_fold(src, s, rows, cols, dst, (hipStream_t)stream),
+                    "awq_fold_inverse_scale launch");
+}
+
 }  // extern "C"

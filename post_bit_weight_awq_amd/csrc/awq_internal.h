@@ -46,6 +46,9 @@ hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const 
 // largest token count of one W4A16 launch (16 tokens per block row of the grid)
 constexpr int64_t kMaxW4Tokens = (int64_t)65535 * 16;
 
+hipError_t launch_fold(const void* src, const float* s, int64_t rows, int64_t cols, void* dst,
+                       hipStream_t stream);
+
 hipError_t launch_pack(const void* W, const float* s, int64_t in_features, int64_t out_features,
                        int32_t* qweight, void* step16, void* zero16, hipStream_t stream);
 

@@ -180,3 +180,17 @@ def test_w4a16_validation(lib):
         a[pos] = ptr
         assert lib.awq_w4a16_matmul(*a) == _lib.AWQ_ERR_INVALID_ARG, pos
         assert lib.awq_last_error()
+
+
+def test_fold_validation(lib):
+    f = lib.awq_fold_inverse_scale
+    assert f(None, FAKE, 4, 1, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 0, 1, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, 4, 0, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p(0x1001), FAKE, 4, 1, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, ctypes.c_void_p(0x1002), 4, 1, ctypes.c_void_p(0x2000), None) \
+        == _lib.AWQ_ERR_INVALID_ARG
+    # dst overlapping src by part of the array
+    assert f(ctypes.c_void_p(0x1000), FAKE, 4, 8, ctypes.c_void_p(0x1010), None) \
+        == _lib.AWQ_ERR_INVALID_ARG
+    assert b"overlap" in lib.awq_last_error()

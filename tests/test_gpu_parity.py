@@ -325,3 +325,32 @@ def test_w4a16_after_gpu_pack(awq):
     qw, st, zr = awq.awq_pack(Wd, res.s_best)
     x = (X[:2].astype(np.float32) / host(res.s_best)[None, :]).astype(np.float16)
     _w4a16_check(awq, x, host(qw), host(st), host(zr))
+
+
+# ------------------------------------------------------ folding 1/s upstream
+@pytest.mark.parametrize("rows,cols", [(5120, 1), (4096, 4096), (37, 13), (64, 8), (3, 1000)])
+def test_fold_bitexact(awq, rows, cols):
+    _say(f"fold {rows}x{cols}")
+    rng = np.random.default_rng(rows + cols)
+    src = (rng.standard_normal((rows, cols)) * rng.choice([1e-5, 1.0, 2e3], (rows, 1))).astype(np.float16)
+    s = rng.uniform(1.6e-4, 50.0, rows).astype(np.float32)
+    s[0] = 1.6e-4                                   # overflow to infinity in fp16
+    src[0, 0] = np.float16(30000.0)
+    want = O.fold_inverse_scale(src if cols > 1 else src[:, 0], s)
+    got = host(awq.awq_fold_inverse_scale(dev(src if cols > 1 else src[:, 0]), dev(s)))
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_fold_in_place_and_unaligned(awq):
+    rng = np.random.default_rng(3)
+    src = rng.standard_normal((17, 24)).astype(np.float16)
+    s = rng.uniform(0.5, 4.0, 17).astype(np.float32)
+    want = O.fold_inverse_scale(src, s)
+    t = dev(src)
+    awq.awq_fold_inverse_scale(t, dev(s), out=t)       # in place, vector path
+    assert np.array_equal(host(t).view(np.uint16), want.view(np.uint16))
+    flat = dev(np.concatenate([np.zeros(1, np.float16), src.ravel()]))
+    view = flat[1:].view(17, 24)                        # 2-byte offset: one element per thread
+    out = torch.empty_like(view)
+    awq.awq_fold_inverse_scale(view, dev(s), out=out)
+    assert np.array_equal(host(out).view(np.uint16), want.view(np.uint16))
