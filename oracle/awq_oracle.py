@@ -371,3 +371,31 @@ def fold_inverse_scale(src16: np.ndarray, s: np.ndarray) -> np.ndarray:
     col = s.reshape((-1,) + (1,) * (a.ndim - 1))
     with np.errstate(over="ignore"):
         return (a.astype(F32) / col).astype(F32).astype(F16)
+
+
+# --------------------------------------------------------------------------
+# saliency ablations
+# --------------------------------------------------------------------------
+def weight_saliency(W: np.ndarray) -> np.ndarray:
+    """Saliency from weight magnitude instead of activations: the mean of
+    |W[o, k]| over output rows ([P1] "How does AWQ decide which weights to
+    protect?" contrasts this choice with activation magnitude).  The same
+    exact column mean as act_stats, taken over W's rows."""
+    return act_stats(np.asarray(W, F16))
+
+
+def select_top_channels(sal: np.ndarray, n_keep: int) -> np.ndarray:
+    """Keep the saliency of the n_keep most salient channels and set the rest
+    to 1, so that only those channels are scaled (s = 1^alpha = 1 elsewhere):
+    the "top ~1% of channels" reading of [P1] (protecting about 1% recovers
+    most of the accuracy) and [P2] (the top 1% weight channels are scaled).
+    Larger saliency first; equal values go to the lower channel index."""
+    sal = np.asarray(sal, F32)
+    n = sal.shape[0]
+    if not 0 <= n_keep <= n:
+        raise ValueError("n_keep outside 0..n")
+    order = np.lexsort((np.arange(n), -sal.astype(F64)))
+    out = np.ones(n, F32)
+    keep = order[:n_keep]
+    out[keep] = sal[keep]
+    return out

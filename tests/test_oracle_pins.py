@@ -472,6 +472,31 @@ def test_fold_into_previous_linear_preserves_the_layer():
     assert np.all(np.abs(yf - y) <= bound)
 
 
+# ------------------------------------------------------- saliency ablations
+def test_weight_saliency_is_the_column_mean_of_abs_w():
+    rng = np.random.default_rng(41)
+    W = (rng.standard_normal((9, 16)) * 0.02).astype(F16)
+    got = O.weight_saliency(W)
+    for k in range(16):
+        m = brute.mean_abs_exact([Fraction(float(v)) for v in W[:, k]])
+        assert Fraction(float(got[k])) == brute.round_rne(brute.round_rne(m, brute.BINARY64),
+                                                          brute.BINARY32)
+
+
+@pytest.mark.parametrize("n_keep", [0, 1, 3, 7, 12])
+def test_select_top_channels_brute_force(n_keep):
+    sal = np.array([0.5, 2.0, 2.0, 0.1, 7.0, 2.0, 0.5, 0.0, 3.0, 2.0, 1e-5, 7.0], F32)
+    got = O.select_top_channels(sal, n_keep)
+    ranked = sorted(range(len(sal)), key=lambda k: (-float(sal[k]), k))[:n_keep]
+    for k in range(len(sal)):
+        assert got[k] == (sal[k] if k in ranked else F32(1.0))
+    # kept channels scale, the others have s = 1 at every grid point
+    s, _ = O.scale_table(got)
+    for k in range(len(sal)):
+        if k not in ranked:
+            assert np.all(s[:, k] == 1.0)
+
+
 def test_literal_division_changes_loss_negligibly():
     """Folding s back by multiplying with fp32(1/s) instead of dividing by s
     moves the dequantized weight by at most one fp16 rounding step."""
