@@ -219,6 +219,25 @@ int awq_w4a16_matmul(const void* X, int64_t n_tokens, int64_t in_features, int64
 int awq_fold_inverse_scale(const void* src, const float* s, int64_t rows, int64_t cols, void* dst,
                            void* stream);
 
+/* ------------------------------------------------------------------------
+ * Saliency ablations.
+ * Weight-magnitude saliency needs no entry of its own: awq_act_stats on W
+ * ([out_features, in_features] in place of X) gives mean_o |W[o, k]|.
+ * Top-n selection: sal_out[k] = sal[k] for the n_keep largest saliencies
+ * (equal values: lower k first) and 1.0f for every other k, so that only the
+ * kept channels are scaled (s = 1^alpha = 1 elsewhere) when sal_out is
+ * passed to awq_search_layer.
+ *   sal, sal_out: [n] fp32, 4-byte aligned; sal_out may be sal (in place)
+ *                 but must not otherwise overlap it; sal must hold no NaN
+ *   0 <= n_keep <= n <= 2^20
+ * Errors: AWQ_ERR_INVALID_ARG (nothing is enqueued); AWQ_ERR_HIP.
+ * Source: dev.to page, "How does AWQ decide which weights to protect?"
+ * (activation versus weight magnitude; protecting about 1% of channels);
+ * esaholic.com page (the top 1% channels are scaled).
+ * ---------------------------------------------------------------------- */
+int awq_select_top_channels(const float* sal, int64_t n, int64_t n_keep, float* sal_out,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ from ._lib import STAGE_ALL, STAGE_GRID, STAGE_PREPARE, STAGE_SELECT  # noqa: F4
 
 __all__ = ["AwqConfig", "AwqError", "default_config", "awq_act_stats",
            "awq_act_stats_workspace_size", "awq_search_plan", "awq_search_workspace_size",
-           "awq_search_layer", "awq_pack", "awq_w4a16_matmul", "awq_fold_inverse_scale", "SearchResult", "load"]
+           "awq_search_layer", "awq_pack", "awq_w4a16_matmul", "awq_fold_inverse_scale", "awq_select_top_channels", "awq_weight_saliency",
+           "SearchResult", "load"]
 
 
 def default_config(n_grid: int = 20, sal_floor: float = 1e-4) -> AwqConfig:
@@ -211,4 +212,24 @@ def awq_fold_inverse_scale(src: torch.Tensor, s: torch.Tensor, *,
         ctypes.c_void_p(_dev(s, "s", torch.float32, (rows,))), rows, cols,
         ctypes.c_void_p(_dev(out, "out", torch.float16, tuple(src.shape))),
         _stream(stream)))
+    return out
+
+
+def awq_weight_saliency(W: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """mean_o |W[o, k]| (weight-magnitude saliency): awq_act_stats over W's rows."""
+    return awq_act_stats(W, out=out, stream=stream)
+
+
+def awq_select_top_channels(sal: torch.Tensor, n_keep: int, *,
+                            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """sal with every channel outside the n_keep most salient set to 1."""
+    if sal.dim() != 1:
+        raise ValueError("sal must be [in_features]")
+    n = sal.shape[0]
+    if out is None:
+        out = torch.empty_like(sal)
+    check(load().awq_select_top_channels(
+        ctypes.c_void_p(_dev(sal, "sal", torch.float32, (n,))), n, int(n_keep),
+        ctypes.c_void_p(_dev(out, "out", torch.float32, (n,))), _stream(stream)))
     return out

@@ -23,6 +23,7 @@ EXPORTS = (
     "awq_act_stats_workspace_size", "awq_act_stats",
     "awq_search_plan_query", "awq_search_workspace_size", "awq_search_layer",
     "awq_search_layer_stages", "awq_pack", "awq_w4a16_matmul", "awq_fold_inverse_scale",
+    "awq_select_top_channels",
 )
 
 
@@ -85,6 +86,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.awq_w4a16_matmul.restype = I32
     lib.awq_fold_inverse_scale.argtypes = [P, P, I64, I64, P, P]
     lib.awq_fold_inverse_scale.restype = I32
+    lib.awq_select_top_channels.argtypes = [P, I64, I64, P, P]
+    lib.awq_select_top_channels.restype = I32
     _lib = lib
     return lib
 

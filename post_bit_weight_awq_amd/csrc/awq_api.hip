@@ -227,4 +227,19 @@ int awq_fold_inverse_scale(const void* src, const float* s, int64_t rows, int64_
                     "awq_fold_inverse_scale launch");
 }
 
+int awq_select_top_channels(const float* sal, int64_t n, int64_t n_keep, float* sal_out,
+                            void* stream) {
+  if (!sal || !sal_out) return fail(AWQ_ERR_INVALID_ARG, "sal/sal_out is NULL");
+  if (n < 1 || n > kMaxFeatures)
+    return fail(AWQ_ERR_INVALID_ARG, "n=%lld outside 1..%lld", (long long)n, (long long)kMaxFeatures);
+  if (n_keep < 0 || n_keep > n)
+    return fail(AWQ_ERR_INVALID_ARG, "n_keep=%lld outside 0..n", (long long)n_keep);
+  if (((uintptr_t)sal & 3u) || ((uintptr_t)sal_out & 3u))
+    return fail(AWQ_ERR_INVALID_ARG, "sal/sal_out must be 4-byte aligned");
+  if (sal != sal_out && sal < sal_out + n && sal_out < sal + n)
+    return fail(AWQ_ERR_INVALID_ARG, "sal and sal_out overlap without being the same array");
+  return hip_result(awq::launch_select_top(sal, n, n_keep, sal_out, (hipStream_t)stream),
+                    "awq_select_top_channels launch");
+}
+
 }  // extern "C"

@@ -49,6 +49,9 @@ constexpr int64_t kMaxW4Tokens = (int64_t)65535 * 16;
 hipError_t launch_fold(const void* src, const float* s, int64_t rows, int64_t cols, void* dst,
                        hipStream_t stream);
 
+hipError_t launch_select_top(const float* sal, int64_t n, int64_t n_keep, float* out,
+                             hipStream_t stream);
+
 hipError_t launch_pack(const void* W, const float* s, int64_t in_features, int64_t out_features,
                        int32_t* qweight, void* step16, void* zero16, hipStream_t stream);
 

@@ -194,3 +194,15 @@ def test_fold_validation(lib):
     assert f(ctypes.c_void_p(0x1000), FAKE, 4, 8, ctypes.c_void_p(0x1010), None) \
         == _lib.AWQ_ERR_INVALID_ARG
     assert b"overlap" in lib.awq_last_error()
+
+
+def test_select_top_validation(lib):
+    f = lib.awq_select_top_channels
+    assert f(None, 8, 1, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, 0, ctypes.c_void_p(0x2000), None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, 9, ctypes.c_void_p(0x2000), None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 8, -1, ctypes.c_void_p(0x2000), None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p(0x1002), 8, 1, ctypes.c_void_p(0x2000), None) \
+        == _lib.AWQ_ERR_INVALID_ARG
+    assert f(ctypes.c_void_p(0x1000), 8, 1, ctypes.c_void_p(0x1004), None) \
+        == _lib.AWQ_ERR_INVALID_ARG

@@ -354,3 +354,30 @@ def test_fold_in_place_and_unaligned(awq):
     out = torch.empty_like(view)
     awq.awq_fold_inverse_scale(view, dev(s), out=out)
     assert np.array_equal(host(out).view(np.uint16), want.view(np.uint16))
+
+
+# ------------------------------------------------------- saliency ablations
+def test_weight_saliency_bitexact(awq):
+    _, _, W = synth.make_layer(2, n_tokens=8, out_features=700)
+    got = host(awq.awq_weight_saliency(dev(W)))
+    assert np.array_equal(got.view(np.uint32), O.weight_saliency(W).view(np.uint32))
+
+
+@pytest.mark.parametrize("n,n_keep", [(4096, 41), (5120, 51), (13824, 138), (100, 0),
+                                      (100, 100), (3000, 1), (2049, 2048), (1, 1)])
+def test_select_top_matches_oracle(awq, n, n_keep):
+    rng = np.random.default_rng(n + n_keep)
+    sal = rng.choice(np.array([0.0, 0.25, 0.5, 3.0, 3.0, 17.0], np.float32), n) \
+        * rng.choice([1.0, 1.0, 1.0, 0.5], n).astype(np.float32)     # many ties
+    sal[rng.integers(0, n, max(1, n // 50))] = rng.uniform(1, 100, max(1, n // 50)).astype(np.float32)
+    got = host(awq.awq_select_top_channels(dev(sal), n_keep))
+    want = O.select_top_channels(sal, n_keep)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_select_top_in_place(awq):
+    _, X, _ = synth.make_layer(2, n_tokens=64, out_features=1)
+    sal = O.act_stats(X)
+    t = dev(sal)
+    awq.awq_select_top_channels(t, 41, out=t)
+    assert np.array_equal(host(t).view(np.uint32), O.select_top_channels(sal, 41).view(np.uint32))
