@@ -286,6 +286,45 @@ def decode_bench(tokens, reps):
     return res
 
 
+def ablation_bench(configs):
+    """Best search loss with four saliency choices on the same seeded layers:
+    activation magnitude (the method), weight magnitude, and each restricted to
+    the top 1% of channels (others unscaled); the loss at alpha = 0 is plain
+    round-to-nearest.  All on the GPU path."""
+    import torch
+    import synth
+    import post_bit_weight_awq_amd as awq
+    awq.load()
+    cfg = awq.default_config()
+    rows = []
+    for c, layer in configs:
+        spec, X, W = synth.make_layer(c, layer)
+        Xd, Wd = torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda()
+        del X, W
+        k = spec.in_features
+        n1 = max(1, round(0.01 * k))
+        sal_a = awq.awq_act_stats(Xd)
+        sal_w = awq.awq_weight_saliency(Wd)
+        choices = {"activation": sal_a, "weight": sal_w,
+                   "activation_top1pct": awq.awq_select_top_channels(sal_a, n1),
+                   "weight_top1pct": awq.awq_select_top_channels(sal_w, n1)}
+        out = {"config": c, "layer": spec.name, "shape": [spec.n_tokens, k, spec.out_features],
+               "top_channels": n1}
+        for name, sal in choices.items():
+            r = awq.awq_search_layer(Xd, Wd, sal, cfg)
+            losses = r.losses.cpu().numpy()
+            b = int(r.best_idx.item())
+            out[name] = {"best_alpha": b / cfg.n_grid, "best_loss": float(losses[b])}
+            out["rtn_loss"] = float(losses[0])
+        for name in choices:
+            out[name]["vs_rtn"] = round(out[name]["best_loss"] / out["rtn_loss"], 4)
+        rows.append(out)
+        log(f"ablation {spec.name}: " + ", ".join(f"{n} {out[n]['vs_rtn']}" for n in choices))
+        del Xd, Wd
+        torch.cuda.empty_cache()
+    return rows
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of a known size (PMC byte-counter scale)."""
     import torch
@@ -309,6 +348,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--ablation", action="store_true",
+                    help="best loss with activation vs weight saliency, all vs top 1% channels")
     ap.add_argument("--decode", action="store_true",
                     help="time the W4A16 product on packed weights (13B block, 1 and 16 tokens)")
     args = ap.parse_args()
@@ -321,6 +362,19 @@ def main():
 
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+
+    if args.ablation:
+        import torch
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            sys.exit(1)
+        cases = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (5, 0), (5, 1), (5, 2), (5, 3)]
+        rows = ablation_bench(cases)
+        print(json.dumps({"metric": "best search loss / round-to-nearest loss per saliency choice",
+                          "unit": "ratio", "higher_is_better": False, "n_gpus": 1,
+                          "data": "synthetic (seeded generators, outlier-channel activations)",
+                          "rows": rows}))
         return
 
     if args.decode:
