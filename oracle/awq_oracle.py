@@ -120,17 +120,23 @@ def _near_half(x: np.ndarray) -> np.ndarray:
     return frac <= np.spacing(np.abs(x).astype(F32)).astype(F64)
 
 
-def quantize(ws: np.ndarray, group: int = GROUP, w_bit: int = W_BIT) -> GroupQuant:
-    """Quantize binary32 rows group-wise to asymmetric w_bit integers.
+def quantize(ws: np.ndarray, group: int = GROUP, w_bit: int = W_BIT,
+             zero_point: bool = True) -> GroupQuant:
+    """Quantize binary32 rows group-wise to w_bit integers.
 
-    [P4] step-size equation: step = (max - min) / (2^b - 1) over a group;
-    [P1] quant_config: zero point on, groups of 128 along in_features;
-    [P3] "How it works", step 4: every group has its own scale.
-
-    Per group (binary32, round half to even):
-        step = (mx - mn) / 15          (a zero range takes step = 1)
+    Asymmetric (zero_point, the method's setting): [P4] step-size equation,
+    step = (max - min) / (2^b - 1) over a group; [P1] quant_config: zero point
+    on, groups of 128 along in_features; [P3] "How it works", step 4: every
+    group has its own scale.  Per group (binary32, round half to even):
+        step = (mx - mn) / (2^b - 1)   (a zero range takes step = 1)
         zero = rint(-mn / step)        (not clamped; -0 becomes +0)
-        q    = clamp(rint(w / step) + zero, 0, 15)
+        q    = clamp(rint(w / step) + zero, 0, 2^b - 1)
+
+    Symmetric (the round-to-nearest baseline of [P1] "Why does naive 4-bit
+    quantization wreck LLM accuracy?": step = max|w| / 2^(b-1), value
+    step * round(w / step)); the rounded value is clamped to the b-bit signed
+    range [-2^(b-1), 2^(b-1) - 1] and stored offset by 2^(b-1), i.e. with the
+    fixed zero point 2^(b-1), so both variants dequantize as (q - zero) step.
     """
     ws = np.asarray(ws)
     if ws.dtype != F32 or ws.ndim != 2 or ws.shape[1] % group:
@@ -140,13 +146,20 @@ def quantize(ws: np.ndarray, group: int = GROUP, w_bit: int = W_BIT) -> GroupQua
     g = ws.reshape(rows, k // group, group)
     mn = g.min(axis=2)
     mx = g.max(axis=2)
-    step = ((mx - mn) / qmax).astype(F32)
-    step = np.where(step == F32(0), F32(1), step).astype(F32)
-    zpre = (-mn / step).astype(F32)
-    zero = (np.rint(zpre) + F32(0)).astype(F32)
+    if zero_point:
+        step = ((mx - mn) / qmax).astype(F32)
+        step = np.where(step == F32(0), F32(1), step).astype(F32)
+        zpre = (-mn / step).astype(F32)
+        zero = (np.rint(zpre) + F32(0)).astype(F32)
+    else:
+        amax = np.maximum(np.abs(mn), np.abs(mx))
+        step = (amax / F32(2 ** (w_bit - 1))).astype(F32)
+        step = np.where(step == F32(0), F32(1), step).astype(F32)
+        zpre = np.zeros_like(step)
+        zero = np.full_like(step, F32(2 ** (w_bit - 1)))
     x = (g / step[:, :, None]).astype(F32)
     q = np.clip(np.rint(x) + zero[:, :, None], F32(0), qmax).astype(F32)
-    tie = _near_half(x) | _near_half(zpre)[:, :, None]
+    tie = _near_half(x) | (_near_half(zpre)[:, :, None] if zero_point else False)
     return GroupQuant(step, zero, q.reshape(rows, k).astype(np.uint8),
                       tie.reshape(rows, k))
 
@@ -186,9 +199,10 @@ def dequantize(gq: GroupQuant, inv_s_row: np.ndarray, group: int = GROUP,
 
 
 def fake_quant(W: np.ndarray, s_row: np.ndarray, inv_s_row: np.ndarray,
-               group: int = GROUP, w_bit: int = W_BIT) -> np.ndarray:
+               group: int = GROUP, w_bit: int = W_BIT, zero_point: bool = True) -> np.ndarray:
     """Q(W diag(s)) diag(s)^-1 as fp16 (steps 3 and 4 together)."""
-    return dequantize(quantize(scaled_weights(W, s_row), group, w_bit), inv_s_row, group)
+    return dequantize(quantize(scaled_weights(W, s_row), group, w_bit, zero_point), inv_s_row,
+                      group)
 
 
 # --------------------------------------------------------------------------
@@ -234,7 +248,8 @@ class SearchResult:
 
 
 def search_layer(X: np.ndarray, W: np.ndarray, sal: np.ndarray, n_grid: int = N_GRID,
-                 floor: float = SAL_FLOOR, group: int = GROUP, w_bit: int = W_BIT) -> SearchResult:
+                 floor: float = SAL_FLOOR, group: int = GROUP, w_bit: int = W_BIT,
+                 zero_point: bool = True) -> SearchResult:
     """The per-layer grid search, in the order of [P1]'s search_scale listing:
     reference output; for each alpha: scale, quantize, fold back, output MSE;
     keep the first strict minimum."""
@@ -243,7 +258,7 @@ def search_layer(X: np.ndarray, W: np.ndarray, sal: np.ndarray, n_grid: int = N_
     y_ref = X64 @ np.asarray(W, F16).astype(F64).T
     losses = np.empty(n_grid, dtype=F64)
     for i in range(n_grid):
-        wq = fake_quant(W, s[i], inv_s[i], group, w_bit)
+        wq = fake_quant(W, s[i], inv_s[i], group, w_bit, zero_point)
         d = X64 @ wq.astype(F64).T - y_ref
         losses[i] = np.mean(d * d)
     best = argmin_first(losses)
@@ -251,7 +266,8 @@ def search_layer(X: np.ndarray, W: np.ndarray, sal: np.ndarray, n_grid: int = N_
 
 
 def tile_sq_error(X: np.ndarray, W: np.ndarray, s_row: np.ndarray, inv_s_row: np.ndarray,
-                  rows: slice, cols: slice, group: int = GROUP, w_bit: int = W_BIT) -> float:
+                  rows: slice, cols: slice, group: int = GROUP, w_bit: int = W_BIT,
+                  zero_point: bool = True) -> float:
     """Sum of squared output differences over a token range x output range.
 
     The same quantity as output_mse restricted to a sub-block (not divided by
@@ -259,7 +275,7 @@ def tile_sq_error(X: np.ndarray, W: np.ndarray, s_row: np.ndarray, inv_s_row: np
     test check a large run one block at a time.
     """
     Wsub = np.asarray(W, F16)[cols]
-    wq = fake_quant(Wsub, s_row, inv_s_row, group, w_bit)
+    wq = fake_quant(Wsub, s_row, inv_s_row, group, w_bit, zero_point)
     X64 = np.asarray(X, F16)[rows].astype(F64)
     d = X64 @ wq.astype(F64).T - X64 @ Wsub.astype(F64).T
     return float(np.sum(d * d))
@@ -299,11 +315,13 @@ def unpack_codes(qweight: np.ndarray) -> np.ndarray:
     return out.reshape(rows, kw * 8)
 
 
-def pack(W: np.ndarray, s_row: np.ndarray, group: int = GROUP, w_bit: int = W_BIT) -> Packed:
+def pack(W: np.ndarray, s_row: np.ndarray, group: int = GROUP, w_bit: int = W_BIT,
+         zero_point: bool = True) -> Packed:
     """Quantize W diag(s) with exact division and pack the codes, with the
     per-group step and zero point stored as fp16 ([P1] quant_config;
-    [P3] worked example: one 16-bit scale per 128 weights)."""
-    gq = quantize(scaled_weights(W, s_row), group, w_bit)
+    [P3] worked example: one 16-bit scale per 128 weights).  Codes of fewer
+    than 4 bits still take one nibble each."""
+    gq = quantize(scaled_weights(W, s_row), group, w_bit, zero_point)
     return Packed(pack_codes(gq.q), gq.step.astype(F16), gq.zero.astype(F16), gq.q, gq.tie)
 
 

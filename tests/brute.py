@@ -60,11 +60,21 @@ def f16_to_fraction(h) -> Fraction:
     return Fraction(float(h))
 
 
-def quantize_group(ws: Sequence[Fraction], qmax: int = 15) -> Tuple[Fraction, Fraction, List[int]]:
+def quantize_group(ws: Sequence[Fraction], qmax: int = 15,
+                   symmetric: bool = False) -> Tuple[Fraction, Fraction, List[int]]:
     """One group, each binary32 operation rounded explicitly:
     step = r32(r32(max - min) / qmax), zero = rint(r32(-min / step)),
-    q = clamp(rint(r32(w / step)) + zero, 0, qmax)."""
+    q = clamp(rint(r32(w / step)) + zero, 0, qmax).
+    Symmetric: step = r32(max|w| / h) and zero = h with h = (qmax + 1) / 2."""
     mn, mx = min(ws), max(ws)
+    if symmetric:
+        h = (qmax + 1) // 2
+        step = round_rne(max(abs(mn), abs(mx)) / h)
+        if step == 0:
+            step = Fraction(1)
+        zero = Fraction(h)
+        q = [int(min(max(rint_even(round_rne(w / step)) + zero, 0), qmax)) for w in ws]
+        return step, zero, q
     step = round_rne(round_rne(mx - mn) / qmax)
     if step == 0:
         step = Fraction(1)
@@ -76,14 +86,15 @@ def quantize_group(ws: Sequence[Fraction], qmax: int = 15) -> Tuple[Fraction, Fr
     return step, zero, q
 
 
-def fake_quant_row(w_row: Sequence[Fraction], s_row: Sequence[Fraction], group: int = 128):
+def fake_quant_row(w_row: Sequence[Fraction], s_row: Sequence[Fraction], group: int = 128,
+                   qmax: int = 15, symmetric: bool = False):
     """Quantize-dequantize one weight row: ws = r32(w s), group quantization,
     t = r32((q - zero) step), wq = r16(t * r32(1/s)).  Returns (wq, codes)."""
     ws = [round_rne(w * s) for w, s in zip(w_row, s_row)]
     wq: List[Fraction] = []
     codes: List[int] = []
     for g0 in range(0, len(ws), group):
-        step, zero, q = quantize_group(ws[g0:g0 + group])
+        step, zero, q = quantize_group(ws[g0:g0 + group], qmax, symmetric)
         for j, qq in enumerate(q):
             t = round_rne((qq - zero) * step)
             inv_s = round_rne(Fraction(1) / s_row[g0 + j])

@@ -99,6 +99,67 @@ def test_losses_match_exact_rationals(seed):
         assert res.losses[i] == pytest.approx(float(exact), rel=1e-12, abs=0)
 
 
+QUANT_VARIANTS = [(32, 4, True), (64, 3, True), (128, 3, False), (64, 4, False), (32, 3, False)]
+
+
+@pytest.mark.parametrize("group,w_bit,zp", QUANT_VARIANTS)
+def test_quantizer_variants_match_exact_rationals(group, w_bit, zp):
+    """Other group sizes, 3-bit codes and the symmetric variant, against the
+    same exact-rational emulation."""
+    X, W = _tiny_case(group + w_bit, k=256, out=3)
+    s, inv_s = O.scale_table(O.act_stats(X))
+    qmax = 2 ** w_bit - 1
+    for i in (0, 11):
+        gq = O.quantize(O.scaled_weights(W, s[i]), group, w_bit, zp)
+        wq = O.dequantize(gq, inv_s[i], group)
+        s_fr = [Fraction(float(v)) for v in s[i]]
+        for r in range(W.shape[0]):
+            bw, bq = brute.fake_quant_row([Fraction(float(v)) for v in W[r]], s_fr, group, qmax,
+                                          not zp)
+            assert bq == gq.q[r].tolist()
+            assert [Fraction(float(v)) for v in wq[r]] == bw
+
+
+@pytest.mark.parametrize("group,w_bit,zp", QUANT_VARIANTS[:3])
+def test_variant_losses_match_exact_rationals(group, w_bit, zp):
+    X, W = _tiny_case(7, n=4, k=128, out=2)
+    res = O.search_layer(X, W, O.act_stats(X), group=group, w_bit=w_bit, zero_point=zp)
+    Xf = [[Fraction(float(v)) for v in row] for row in X]
+    Wf = [[Fraction(float(v)) for v in row] for row in W]
+    for i in (0, 9):
+        s_fr = [Fraction(float(v)) for v in res.s[i]]
+        Wq = [brute.fake_quant_row(row, s_fr, group, 2 ** w_bit - 1, not zp)[0] for row in Wf]
+        assert res.losses[i] == pytest.approx(float(brute.mse_exact(Xf, Wf, Wq)), rel=1e-12)
+
+
+def test_symmetric_rtn_worked_group():
+    """The round-to-nearest formula of the dev.to page on a group whose values
+    are multiples of step = max|w| / 8 in [-8, 7] steps: every value is stored
+    exactly (codes k + 8); a value of +8 steps would clamp to code 15."""
+    k = np.array([(j % 16) - 8 for j in range(128)], dtype=np.int64)
+    k[5] = -8                                     # max|w| = 8 steps, at a negative value
+    w = (k / 64.0).astype(F16)[None, :]           # step = 8/64 / 8 = 1/64
+    p = O.pack(w, np.ones(128, F32), zero_point=False)
+    assert float(p.step16[0, 0]) == 1 / 64 and float(p.zero16[0, 0]) == 8
+    assert np.array_equal(p.q[0].astype(np.int64), k + 8)
+    assert np.array_equal(O.dequant_packed(p.qweight, p.step16, p.zero16)[0], w[0].astype(F64))
+    w2 = w.copy()
+    w2[0, 7] = F16(8 / 64.0)                      # +8 steps: outside the signed 4-bit range
+    p2 = O.pack(w2, np.ones(128, F32), zero_point=False)
+    assert p2.q[0, 7] == 15 and float(p2.step16[0, 0]) == 1 / 64
+
+
+def test_three_bit_grid_group():
+    """Step-size equation with 2^3 - 1 levels: a group spanning 7 steps is
+    stored exactly."""
+    u = np.array([(j % 8) - 3 for j in range(128)], dtype=np.int64)
+    w = (u / 32.0).astype(F16)[None, :]
+    p = O.pack(w, np.ones(128, F32), w_bit=3)
+    assert float(p.step16[0, 0]) == 1 / 32 and float(p.zero16[0, 0]) == 3
+    assert int(p.q.max()) == 7
+    assert np.array_equal(O.dequant_packed(p.qweight, p.step16, p.zero16)[0], w[0].astype(F64))
+
+
 def test_tile_squared_error_matches_exact_rationals():
     """The per-block squared error that full-size parity samples: each block
     equals the exact rational sum over that block, and the blocks of a
@@ -522,8 +583,8 @@ def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
     elif mutation == "symmetric_step":
         orig = O.quantize
 
-        def sym(ws, group=128, w_bit=4):
-            gq = orig(ws, group, w_bit)
+        def sym(ws, group=128, w_bit=4, zero_point=True):
+            gq = orig(ws, group, w_bit, zero_point)
             g = ws.reshape(ws.shape[0], -1, group)
             gq.step = (np.abs(g).max(axis=2) / F32(8)).astype(F32)
             return gq
@@ -554,8 +615,8 @@ def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
     elif mutation == "no_zero_canon":
         orig = O.quantize
 
-        def negz(ws, group=128, w_bit=4):
-            gq = orig(ws, group, w_bit)
+        def negz(ws, group=128, w_bit=4, zero_point=True):
+            gq = orig(ws, group, w_bit, zero_point)
             gq.zero = np.where(gq.zero == 0, F32(-0.0), gq.zero)
             return gq
         monkeypatch.setattr(O, "quantize", negz)
