@@ -61,14 +61,21 @@ typedef enum awq_status {
 
 /* Quantization settings (the quant_config of the dev.to page's "What do you
  * actually deploy" section, plus the search_scale listing's grid size and
- * saliency floor).  Only w_bit = 4, group_size = 128 and zero_point = 1 are
- * implemented; n_grid may be 1..64; sal_floor must be finite and > 0. */
+ * saliency floor).  The method's setting is {4, 128, 20, 1e-4f, 1}.  Also
+ * implemented, as ablations: w_bit = 3 (codes still one per nibble), group
+ * sizes 64 and 32 (the dev.to page: finer groups trade scale storage for
+ * accuracy), and zero_point = 0, the symmetric round-to-nearest of the dev.to
+ * page's "Why does naive 4-bit quantization wreck LLM accuracy?":
+ * step = max|w| / 2^(w_bit-1), codes clamped to the signed range and stored
+ * with the fixed zero 2^(w_bit-1).  Other values give AWQ_ERR_UNSUPPORTED.
+ * n_grid may be 1..64; sal_floor must be finite and > 0.  in_features must be
+ * a multiple of 128 for every group size. */
 typedef struct awq_config {
-  int32_t w_bit;      /* bits per code: 4                                  */
-  int32_t group_size; /* weights per step/zero along in_features: 128      */
+  int32_t w_bit;      /* bits per code: 4 (or 3)                           */
+  int32_t group_size; /* weights per step/zero along in_features: 128 (or 64, 32) */
   int32_t n_grid;     /* grid points alpha_i = i / n_grid: default 20      */
   float sal_floor;    /* saliency clamp before the power: default 1e-4f    */
-  int32_t zero_point; /* asymmetric quantization with a zero point: 1      */
+  int32_t zero_point; /* 1: asymmetric with a zero point; 0: symmetric     */
 } awq_config;
 
 /* Fills *cfg with the defaults {4, 128, 20, 1e-4f, 1}. */
@@ -106,7 +113,7 @@ int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* s
  *   losses_out:   [n_grid] float64: L_i, the mean squared output error
  *   best_idx_out: [1] int32: i*, or -1 when no L_i is finite
  *   s_best_out:   [in_features] fp32: s_i* (all NaN when i* = -1)
- *   in_features must be a multiple of group_size; n_tokens, out_features >= 1.
+ *   in_features must be a multiple of 128; n_tokens, out_features >= 1.
  * The workspace (size from awq_search_workspace_size) holds the scale table,
  * the per-group quantizer parameters and the per-tile partial sums;
  * awq_search_plan describes where.  The squared output error is formed as
@@ -165,7 +172,9 @@ int awq_search_layer_stages(int stage_mask, const void* X, const void* W, const 
  *                 of word w holds the code of column 8w + j
  *   step_out:     [out_features, in_features / group_size] fp16
  *   zero_out:     [out_features, in_features / group_size] fp16 (integer values)
- * A group whose values are all equal takes step = 1.
+ * A group whose values are all equal takes step = 1.  Codes follow cfg's
+ * bit width and zero-point setting (3-bit codes take one nibble each);
+ * in_features must be a multiple of 128.
  * Source: esaholic.com page, "INT4 Weight Packing & Export"; dev.to page,
  * quant_config; modelrefs.com page, memory example (one 16-bit scale per 128).
  * ---------------------------------------------------------------------- */

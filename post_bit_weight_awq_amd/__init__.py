@@ -28,11 +28,17 @@ __all__ = ["AwqConfig", "AwqError", "default_config", "awq_act_stats",
            "SearchResult", "load"]
 
 
-def default_config(n_grid: int = 20, sal_floor: float = 1e-4) -> AwqConfig:
+def default_config(n_grid: int = 20, sal_floor: float = 1e-4, *, group_size: int = 128,
+                   w_bit: int = 4, zero_point: bool = True) -> AwqConfig:
+    """The method's settings (4-bit, groups of 128, zero point, 20 grid points,
+    floor 1e-4); the keywords select the ablation variants the library has."""
     cfg = AwqConfig()
     load().awq_default_config(ctypes.byref(cfg))
     cfg.n_grid = n_grid
     cfg.sal_floor = sal_floor
+    cfg.group_size = group_size
+    cfg.w_bit = w_bit
+    cfg.zero_point = 1 if zero_point else 0
     return cfg
 
 

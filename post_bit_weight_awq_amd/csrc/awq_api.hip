@@ -34,11 +34,13 @@ constexpr int64_t kMaxWeights = (int64_t)1 << 34;  // one work-item per 8 weight
 
 int check_config(const awq_config* cfg) {
   if (!cfg) return fail(AWQ_ERR_INVALID_ARG, "cfg is NULL");
-  if (cfg->w_bit != 4) return fail(AWQ_ERR_UNSUPPORTED, "w_bit=%d: only 4 is implemented", cfg->w_bit);
-  if (cfg->group_size != 128)
-    return fail(AWQ_ERR_UNSUPPORTED, "group_size=%d: only 128 is implemented", cfg->group_size);
-  if (cfg->zero_point != 1)
-    return fail(AWQ_ERR_UNSUPPORTED, "zero_point=%d: only asymmetric (1) is implemented",
+  if (cfg->w_bit != 4 && cfg->w_bit != 3)
+    return fail(AWQ_ERR_UNSUPPORTED, "w_bit=%d: 3 and 4 are implemented", cfg->w_bit);
+  if (cfg->group_size != 128 && cfg->group_size != 64 && cfg->group_size != 32)
+    return fail(AWQ_ERR_UNSUPPORTED, "group_size=%d: 32, 64 and 128 are implemented",
+                cfg->group_size);
+  if (cfg->zero_point != 1 && cfg->zero_point != 0)
+    return fail(AWQ_ERR_UNSUPPORTED, "zero_point=%d: 1 (asymmetric) or 0 (symmetric)",
                 cfg->zero_point);
   if (cfg->n_grid < 1 || cfg->n_grid > 64)
     return fail(AWQ_ERR_INVALID_ARG, "n_grid=%d outside 1..64", cfg->n_grid);
@@ -68,6 +70,14 @@ int check_ptr(const void* p, const char* name) {
   if (!p) return fail(AWQ_ERR_INVALID_ARG, "%s is NULL", name);
   if (!aligned16(p)) return fail(AWQ_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
   return AWQ_OK;
+}
+
+awq::QuantSpec quant_spec(const awq_config* cfg) {
+  awq::QuantSpec q;
+  q.group = cfg->group_size;
+  q.w_bit = cfg->w_bit;
+  q.zero_point = cfg->zero_point != 0;
+  return q;
 }
 
 int hip_result(hipError_t e, const char* what) {
@@ -116,9 +126,10 @@ int awq_search_plan_query(int64_t n_tokens, int64_t in_features, int64_t out_fea
                           const awq_config* cfg, awq_search_plan* plan) {
   int rc;
   if ((rc = check_config(cfg))) return rc;
-  if ((rc = check_dims(n_tokens, in_features, out_features, true, true, cfg->group_size))) return rc;
+  if ((rc = check_dims(n_tokens, in_features, out_features, true, true, 128))) return rc;
   if (!plan) return fail(AWQ_ERR_INVALID_ARG, "plan is NULL");
-  const awq::SearchPlan p = awq::search_plan(n_tokens, in_features, out_features, cfg->n_grid);
+  const awq::SearchPlan p = awq::search_plan(n_tokens, in_features, out_features, cfg->n_grid,
+                                                 quant_spec(cfg));
   if (p.grid_blocks > awq::kMaxGridBlocks)
     return fail(AWQ_ERR_INVALID_ARG, "layer too large for one search launch (%lld tiles)",
                 (long long)(p.n_t_tiles * p.n_o_tiles));
@@ -158,13 +169,14 @@ int awq_search_layer_stages(int stage_mask, const void* X, const void* W, const 
     return fail(AWQ_ERR_INVALID_ARG, "stage_mask=%d: must be a non-empty OR of AWQ_STAGE_*",
                 stage_mask);
   if ((rc = check_config(cfg))) return rc;
-  if ((rc = check_dims(n_tokens, in_features, out_features, true, true, cfg->group_size))) return rc;
+  if ((rc = check_dims(n_tokens, in_features, out_features, true, true, 128))) return rc;
   if ((rc = check_ptr(X, "X")) || (rc = check_ptr(W, "W")) || (rc = check_ptr(sal, "sal")) ||
       (rc = check_ptr(losses_out, "losses_out")) ||
       (rc = check_ptr(s_best_out, "s_best_out")) || (rc = check_ptr(workspace, "workspace")))
     return rc;
   if (!best_idx_out) return fail(AWQ_ERR_INVALID_ARG, "best_idx_out is NULL");
-  const awq::SearchPlan p = awq::search_plan(n_tokens, in_features, out_features, cfg->n_grid);
+  const awq::SearchPlan p = awq::search_plan(n_tokens, in_features, out_features, cfg->n_grid,
+                                                 quant_spec(cfg));
   if (p.grid_blocks > awq::kMaxGridBlocks)
     return fail(AWQ_ERR_INVALID_ARG, "layer too large for one search launch (%lld tiles)",
                 (long long)(p.n_t_tiles * p.n_o_tiles));
@@ -181,15 +193,15 @@ int awq_pack(const void* W, const float* s, int64_t in_features, int64_t out_fea
              void* stream) {
   int rc;
   if ((rc = check_config(cfg))) return rc;
-  if ((rc = check_dims(1, in_features, out_features, false, true, cfg->group_size))) return rc;
+  if ((rc = check_dims(1, in_features, out_features, false, true, 128))) return rc;
   if ((rc = check_ptr(W, "W")) || (rc = check_ptr(s, "s")) ||
       (rc = check_ptr(qweight_out, "qweight_out")))
     return rc;
   if (!step_out || !zero_out) return fail(AWQ_ERR_INVALID_ARG, "step_out/zero_out is NULL");
   if (((uintptr_t)step_out & 1u) || ((uintptr_t)zero_out & 1u))
     return fail(AWQ_ERR_INVALID_ARG, "step_out/zero_out must be 2-byte aligned");
-  return hip_result(awq::launch_pack(W, s, in_features, out_features, qweight_out, step_out,
-                                     zero_out, (hipStream_t)stream),
+  return hip_result(awq::launch_pack(W, s, in_features, out_features, quant_spec(cfg), qweight_out,
+                                     step_out, zero_out, (hipStream_t)stream),
                     "awq_pack launch");
 }
 

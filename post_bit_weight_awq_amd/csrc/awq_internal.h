@@ -20,22 +20,32 @@ StatsPlan stats_plan(int64_t n_tokens, int64_t in_features);
 hipError_t launch_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal,
                             void* workspace, hipStream_t stream);
 
+// Quantizer settings: group of 32, 64 or 128 columns, 3- or 4-bit codes,
+// zero point (asymmetric) or symmetric.
+struct QuantSpec {
+  int group = 128;
+  int w_bit = 4;
+  bool zero_point = true;
+};
+
 struct SearchPlan {
   int64_t tile_m, tile_n;        // tokens x outputs per tile
   int64_t n_t_tiles, n_o_tiles;  // tile counts
   int kernel;                    // which tile kernel variant
   int64_t grid_blocks;           // blocks of the grid-kernel launch
+  QuantSpec quant;
   size_t off_partials, off_s, off_inv_s, off_params;
   size_t bytes;
 };
-SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid);
+SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid,
+                       const QuantSpec& qs);
 hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t n_tokens,
                          int64_t in_features, int64_t out_features, int n_grid, float sal_floor,
                          double* losses, int32_t* best_idx, float* s_best, void* workspace,
                          const SearchPlan& plan, int stage_mask, hipStream_t stream);
 
 int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid);
-void launch_grid(int tile_m, const void* X, const void* W, const float* s_tab,
+void launch_grid(int tile_m, int group, const void* X, const void* W, const float* s_tab,
                  const float* inv_tab, const GroupParams* prm, double* partials, int64_t N,
                  int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream);
 // largest grid the grid kernel is launched with (blocks of 256 threads in x)
@@ -53,6 +63,7 @@ hipError_t launch_select_top(const float* sal, int64_t n, int64_t n_keep, float*
                              hipStream_t stream);
 
 hipError_t launch_pack(const void* W, const float* s, int64_t in_features, int64_t out_features,
-                       int32_t* qweight, void* step16, void* zero16, hipStream_t stream);
+                       const QuantSpec& qs, int32_t* qweight, void* step16, void* zero16,
+                       hipStream_t stream);
 
 }  // namespace awq

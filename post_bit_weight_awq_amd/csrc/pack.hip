@@ -3,12 +3,13 @@
 // containers; dev.to page, quant_config: zero point, groups of 128, 4 bit;
 // "AWQ > Salient Weight Preservation", step-size equation).
 //
-// HBM-bound: 2 bytes of W in, 0.5 + 4/128 bytes out per weight.  A team of 16
-// lanes owns a (row, group) at a time; each lane loads its 8 weights with one
-// 16-byte load, so a wavefront streams 1 KiB of W per pair it holds.  Per
-// group, in binary32:
-//   ws = w * s, step = (max - min) / 15 (1 for a zero range),
-//   zero = rint(-min / step), q = clamp(rint(ws / step) + zero, 0, 15).
+// HBM-bound: 2 bytes of W in, 0.5 + 4/G bytes out per weight.  A team of G/8
+// lanes owns a (row, group of G columns) at a time; each lane loads its 8
+// weights with one 16-byte load, so a wavefront streams 1 KiB of W per pair
+// set it holds.  Per group, in binary32 (qmax = 2^b - 1):
+//   ws = w * s, step = (max - min) / qmax (1 for a zero range),
+//   zero = rint(-min / step), q = clamp(rint(ws / step) + zero, 0, qmax);
+// the symmetric variant takes step = max|ws| / 2^(b-1) and zero = 2^(b-1).
 // The code needs the correctly rounded quotient ws / step.  It is formed as
 // ws * (1/step), which is within 2.5 ulp of that quotient; the two can round
 // to different integers only when the product lies that close to a
@@ -18,27 +19,32 @@
 
 namespace awq {
 
-// Each team takes kPackPerTeam (row, group) pairs, 16 teams apart, and issues
-// all their loads before any arithmetic, so every lane keeps 64 bytes of W in
-// flight.
+// Each team takes kPackPerTeam (row, group) pairs, a block's worth of teams
+// apart, and issues all their loads before any arithmetic, so every lane
+// keeps 64 bytes of W in flight.  A group of G columns takes a team of G/8
+// lanes.  The code range and zero follow the quantizer settings: qmax =
+// 2^b - 1, and either step = (max - min) / qmax with zero = rint(-min/step),
+// or (symmetric) step = max|w| / 2^(b-1) with zero = 2^(b-1).
 constexpr int kPackPerTeam = 4;
-constexpr int kPackPairsPerBlock = 16 * kPackPerTeam;
 
+template <int G>
 __global__ void __launch_bounds__(256)
 k_pack(const uint4* __restrict__ W, const float* __restrict__ s, int64_t OUT, int64_t K,
-       uint32_t* __restrict__ qweight, _Float16* __restrict__ step16,
+       float qmax, int symmetric, uint32_t* __restrict__ qweight, _Float16* __restrict__ step16,
        _Float16* __restrict__ zero16) {
-  const int64_t ng = K / kGroup;
+  constexpr int TL = G / 8;              // lanes per team
+  constexpr int TEAMS = 256 / TL;        // teams per block
+  const int64_t ng = K / G;
   const int64_t pairs = OUT * ng;
-  const int l16 = threadIdx.x % 16;
-  const int64_t p0 = (int64_t)blockIdx.x * kPackPairsPerBlock + threadIdx.x / 16;
+  const int lt = threadIdx.x % TL;
+  const int64_t p0 = (int64_t)blockIdx.x * (TEAMS * kPackPerTeam) + threadIdx.x / TL;
   uint4 w[kPackPerTeam];
   int64_t k0[kPackPerTeam], widx[kPackPerTeam];
 #pragma unroll
   for (int u = 0; u < kPackPerTeam; ++u) {
-    const int64_t p = min(p0 + 16 * u, pairs - 1);  // a tail team re-reads the last pair
+    const int64_t p = min(p0 + TEAMS * u, pairs - 1);  // a tail team re-reads the last pair
     const int64_t o = p / ng, g = p - o * ng;
-    k0[u] = g * kGroup + l16 * 8;
+    k0[u] = g * G + lt * 8;
     widx[u] = (o * K + k0[u]) / 8;
     w[u] = W[widx[u]];
   }
@@ -61,13 +67,21 @@ k_pack(const uint4* __restrict__ W, const float* __restrict__ s, int64_t OUT, in
       mx = fmaxf(mx, ws[j]);
     }
 #pragma unroll
-    for (int d = 8; d >= 1; d >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, d, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, d, 16));
+    for (int d = TL / 2; d >= 1; d >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, d, TL));
+      mx = fmaxf(mx, __shfl_xor(mx, d, TL));
     }
-    float step = (mx - mn) / 15.0f;
-    if (step == 0.0f) step = 1.0f;
-    const float z = rintf(-mn / step) + 0.0f;
+    float step, z;
+    if (symmetric) {
+      const float half = 0.5f * (qmax + 1.0f);
+      step = fmaxf(fabsf(mn), fabsf(mx)) / half;
+      if (step == 0.0f) step = 1.0f;
+      z = half;
+    } else {
+      step = (mx - mn) / qmax;
+      if (step == 0.0f) step = 1.0f;
+      z = rintf(-mn / step) + 0.0f;
+    }
     const float inv_step = 1.0f / step;
     uint32_t word = 0;
 #pragma unroll
@@ -76,13 +90,13 @@ k_pack(const uint4* __restrict__ W, const float* __restrict__ s, int64_t OUT, in
       float r = rintf(xf);
       // near a half-integer: redo with the exact quotient
       if (0.5f - fabsf(xf - r) <= fabsf(xf) * 0x1p-21f) r = rintf(ws[j] / step);
-      const float q = fminf(fmaxf(r + z, 0.0f), 15.0f);
+      const float q = fminf(fmaxf(r + z, 0.0f), qmax);
       word |= (uint32_t)q << (4 * j);
     }
-    const int64_t p = p0 + 16 * u;
+    const int64_t p = p0 + TEAMS * u;
     if (p < pairs) {
       qweight[widx[u]] = word;
-      if (l16 == 0) {
+      if (lt == 0) {
         step16[p] = (_Float16)step;
         zero16[p] = (_Float16)z;
       }
@@ -90,12 +104,24 @@ k_pack(const uint4* __restrict__ W, const float* __restrict__ s, int64_t OUT, in
   }
 }
 
-hipError_t launch_pack(const void* W, const float* s, int64_t K, int64_t OUT, int32_t* qweight,
-                       void* step16, void* zero16, hipStream_t stream) {
-  const int64_t pairs = OUT * (K / kGroup);
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)((pairs + kPackPairsPerBlock - 1) / kPackPairsPerBlock)),
-                     dim3(256), 0, stream, (const uint4*)W, s, OUT, K, (uint32_t*)qweight,
-                     (_Float16*)step16, (_Float16*)zero16);
+hipError_t launch_pack(const void* W, const float* s, int64_t K, int64_t OUT, const QuantSpec& qs,
+                       int32_t* qweight, void* step16, void* zero16, hipStream_t stream) {
+  const int64_t pairs = OUT * (K / qs.group);
+  const float qmax = (float)((1 << qs.w_bit) - 1);
+  const int sym = qs.zero_point ? 0 : 1;
+  const int per_block = 256 / (qs.group / 8) * kPackPerTeam;
+  const dim3 grid((unsigned)((pairs + per_block - 1) / per_block));
+  const uint4* Wv = (const uint4*)W;
+  uint32_t* qw = (uint32_t*)qweight;
+  _Float16* st = (_Float16*)step16;
+  _Float16* zr = (_Float16*)zero16;
+  if (qs.group == 32)
+    hipLaunchKernelGGL(k_pack<32>, grid, dim3(256), 0, stream, Wv, s, OUT, K, qmax, sym, qw, st, zr);
+  else if (qs.group == 64)
+    hipLaunchKernelGGL(k_pack<64>, grid, dim3(256), 0, stream, Wv, s, OUT, K, qmax, sym, qw, st, zr);
+  else
+    hipLaunchKernelGGL(k_pack<128>, grid, dim3(256), 0, stream, Wv, s, OUT, K, qmax, sym, qw, st,
+                       zr);
   return hipGetLastError();
 }
 

@@ -42,24 +42,29 @@ k_scale_table(const float* __restrict__ sal, float* __restrict__ s_tab,
 }
 
 // ------------------------------------------------- per-group quantizer params
-// A team of 4 lanes owns one (row, group of 128); each lane holds 32 of the
-// group's weights for the whole grid loop.  The 16 teams of a wavefront share
+// A team of 4 lanes owns one (row, group of G = 32, 64 or 128 columns); each
+// lane holds G/4 of the group's weights for the whole grid loop.  The 16 teams of a wavefront share
 // the group and take consecutive rows; a block covers 64 rows.  The block first
 // copies the group's scales for every grid point into LDS (one coalesced pass
 // over the scale table), so the grid loop only reads LDS.
-// Per grid point: ws = fp32(w s), min and max over the group, then
-// step = (max - min) / 15 with IEEE division (1 for a zero range),
-// zero = rint(-min / step) (+0 for a zero), 1/step, and the clamp bounds.
+// Per grid point: ws = fp32(w s), min and max over the group, then with
+// qmax = 2^b - 1 and IEEE divisions (a zero range takes step 1):
+//   zero point:  step = (max - min) / qmax, zero = rint(-min / step) (+0 for 0)
+//   symmetric:   step = max(|min|, |max|) / 2^(b-1), zero = 2^(b-1)
+// then 1/step and the clamp bounds -zero and qmax - zero.
 // Grid points go in blocks of four: after the team's min/max reductions every
 // lane of the team holds all four (min, max) pairs, and lane j of the team
 // finishes grid point i0 + j, so the three divisions run on all lanes at once.
 // Records are written in the layout [grid point][group][row].
 constexpr int kParamsRows = 64;
-// LDS copy of one grid point's 128 scales: four 32-float chunks (one per team
+// LDS copy of one grid point's G scales: four G/4-float chunks (one per team
 // lane), each padded by 4 floats so the four chunks a wavefront reads at once
 // sit in different banks.
-constexpr int kParamsChunk = 36;
-constexpr int kParamsPerGrid = 4 * kParamsChunk;
+template <int G>
+struct ParamsLds {
+  static constexpr int kChunk = G / 4 + 4;
+  static constexpr int kPerGrid = 4 * kChunk;
+};
 
 __device__ __forceinline__ float min3f(float a, float b, float c) {
   float r;
@@ -85,35 +90,42 @@ __device__ __forceinline__ float quad_max_step(float x) {
   return max3f(x, y, y);
 }
 
+template <int G>
 __global__ void __launch_bounds__(256)
 k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
-               GroupParams* __restrict__ prm, int OUT, int K, int n_grid) {
-  extern __shared__ float4 s_lds4[];  // [n_grid][4 chunks][9 float4]
-  const int ngroups = K >> 7;
+               GroupParams* __restrict__ prm, int OUT, int K, int n_grid, float qmax,
+               int symmetric) {
+  constexpr int PL = G / 4;                      // weights per lane
+  constexpr int CH4 = ParamsLds<G>::kChunk / 4;  // float4 per padded chunk
+  constexpr int PG4 = ParamsLds<G>::kPerGrid / 4;
+  constexpr int C4 = G / 4;                      // float4 of scales per group
+  extern __shared__ float4 s_lds4[];             // [n_grid][4 chunks][CH4 float4]
+  const int ngroups = K / G;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int l4 = tid & 3;
   const int o_raw = blockIdx.x * kParamsRows + (tid >> 2);
   const bool live = o_raw < OUT;
   const int o = live ? o_raw : OUT - 1;
-  const int k0 = g * kGroup + l4 * 32;
+  const int k0 = g * G + l4 * PL;
 
   // scales of this group, every grid point: element e = (i, 16-byte column c4)
-  for (int e = tid; e < n_grid * 32; e += 256) {
-    const int i = e >> 5, c4 = e & 31;
-    const float4 v = ((const float4*)(s_tab + (size_t)i * K + g * kGroup))[c4];
-    s_lds4[i * (kParamsPerGrid / 4) + (c4 >> 3) * (kParamsChunk / 4) + (c4 & 7)] = v;
+  for (int e = tid; e < n_grid * C4; e += 256) {
+    const int i = e / C4, c4 = e - i * C4;
+    const float4 v = ((const float4*)(s_tab + (size_t)i * K + g * G))[c4];
+    s_lds4[i * PG4 + (c4 / (PL / 4)) * CH4 + c4 % (PL / 4)] = v;
   }
   const uint4* wp = (const uint4*)(W + (size_t)o * K + k0);
-  uint32_t w[16];
+  uint32_t w[PL / 2];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < PL / 8; ++v) {
     const uint4 t = wp[v];
     w[4 * v] = t.x;
     w[4 * v + 1] = t.y;
     w[4 * v + 2] = t.z;
     w[4 * v + 3] = t.w;
   }
+  const float half = 0.5f * (qmax + 1.0f);  // 2^(b-1)
   __syncthreads();
   const float nz = neg_zero();
   for (int i0 = 0; i0 < n_grid; i0 += 4) {
@@ -121,10 +133,10 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = min(i0 + j, n_grid - 1);
-      const float4* sp = s_lds4 + i * (kParamsPerGrid / 4) + l4 * (kParamsChunk / 4);
+      const float4* sp = s_lds4 + i * PG4 + l4 * CH4;
       float mn, mx;
 #pragma unroll
-      for (int v = 0; v < 8; ++v) {
+      for (int v = 0; v < PL / 4; ++v) {
         const float4 sv = sp[v];
         const float a = mul_f16_f32<false>(w[2 * v], sv.x, nz);
         const float b = mul_f16_f32<true>(w[2 * v], sv.y, nz);
@@ -161,20 +173,25 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     const float mx = l4 == 0 ? mxv[0] : l4 == 1 ? mxv[1] : l4 == 2 ? mxv[2] : mxv[3];
     const int i = i0 + l4;
     if (live && i < n_grid) {
-      float step = (mx - mn) / 15.0f;
-      if (step == 0.0f) step = 1.0f;
-      const float z = rintf(-mn / step) + 0.0f;
+      float step, z;
+      if (symmetric) {
+        step = fmaxf(fabsf(mn), fabsf(mx)) / half;
+        if (step == 0.0f) step = 1.0f;
+        z = half;
+      } else {
+        step = (mx - mn) / qmax;
+        if (step == 0.0f) step = 1.0f;
+        z = rintf(-mn / step) + 0.0f;
+      }
       GroupParams p;
       p.step = step;
       p.inv_step = 1.0f / step;
       p.lo = -z;
-      p.hi = 15.0f - z;
+      p.hi = qmax - z;
       prm[((size_t)i * ngroups + g) * OUT + o] = p;
     }
   }
 }
-
-size_t group_params_lds_bytes(int n_grid) { return sizeof(float) * kParamsPerGrid * n_grid; }
 
 // -------------------------------------------------------------------- argmin
 // 1024 threads: wavefront w sums the partials of grid points w, w+16, ... in
@@ -231,9 +248,11 @@ namespace {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
-SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid) {
+SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid,
+                       const QuantSpec& qs) {
   SearchPlan p;
   p.tile_m = grid_tile_m(n_tokens, out_features, n_grid);
+  p.quant = qs;
   p.tile_n = kGridBN;
   p.kernel = 0;
   p.n_t_tiles = (n_tokens + p.tile_m - 1) / p.tile_m;
@@ -247,7 +266,7 @@ SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_featur
   p.off_inv_s = off;
   off = align256(off + sizeof(float) * (size_t)n_grid * in_features);
   p.off_params = off;
-  off = align256(off + sizeof(GroupParams) * (size_t)n_grid * out_features * (in_features / kGroup));
+  off = align256(off + sizeof(GroupParams) * (size_t)n_grid * out_features * (in_features / qs.group));
   p.bytes = off;
   return p;
 }
@@ -261,19 +280,32 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
   float* s_tab = (float*)(ws + p.off_s);
   float* inv_tab = (float*)(ws + p.off_inv_s);
   GroupParams* prm = (GroupParams*)(ws + p.off_params);
-  const int64_t ng = K / kGroup;
+  const int G = p.quant.group;
+  const int64_t ng = K / G;
+  const float qmax = (float)((1 << p.quant.w_bit) - 1);
+  const int sym = p.quant.zero_point ? 0 : 1;
 
   if (stage_mask & 1) {  // prepare
     const int64_t nst = (int64_t)n_grid * K;
     hipLaunchKernelGGL(k_scale_table, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, stream,
                        sal, s_tab, inv_tab, K, n_grid, sal_floor);
-    hipLaunchKernelGGL(k_group_params,
-                       dim3((unsigned)((OUT + kParamsRows - 1) / kParamsRows), (unsigned)ng),
-                       dim3(256), group_params_lds_bytes(n_grid), stream, (const _Float16*)W,
-                       s_tab, prm, (int)OUT, (int)K, n_grid);
+    const dim3 pgrid((unsigned)((OUT + kParamsRows - 1) / kParamsRows), (unsigned)ng);
+    const _Float16* Wh = (const _Float16*)W;
+    if (G == 32)
+      hipLaunchKernelGGL(k_group_params<32>, pgrid, dim3(256),
+                         sizeof(float) * ParamsLds<32>::kPerGrid * n_grid, stream, Wh, s_tab, prm,
+                         (int)OUT, (int)K, n_grid, qmax, sym);
+    else if (G == 64)
+      hipLaunchKernelGGL(k_group_params<64>, pgrid, dim3(256),
+                         sizeof(float) * ParamsLds<64>::kPerGrid * n_grid, stream, Wh, s_tab, prm,
+                         (int)OUT, (int)K, n_grid, qmax, sym);
+    else
+      hipLaunchKernelGGL(k_group_params<128>, pgrid, dim3(256),
+                         sizeof(float) * ParamsLds<128>::kPerGrid * n_grid, stream, Wh, s_tab,
+                         prm, (int)OUT, (int)K, n_grid, qmax, sym);
   }
   if (stage_mask & 2) {  // grid
-    launch_grid((int)p.tile_m, X, W, s_tab, inv_tab, prm, partials, N, K, OUT, p.n_t_tiles,
+    launch_grid((int)p.tile_m, G, X, W, s_tab, inv_tab, prm, partials, N, K, OUT, p.n_t_tiles,
                 p.n_o_tiles, n_grid, stream);
   }
   if (stage_mask & 4) {  // select

@@ -32,7 +32,9 @@
 //     step's 32 scales and reciprocals travel with the raw tile into LDS and
 //     are read as wavefront-wide broadcasts (no scalar loads in the loop:
 //     they would share the LDS wait counter and force full drains); each
-//     row's group parameters load once per 128 columns.
+//     row's group parameters load once per quantization group (GS steps of
+//     32 columns: a whole group ahead for groups of 128, one step ahead in
+//     two rolling register sets for groups of 32 and 64).
 //     The production cost is spread over the BM tokens of the tile.
 //   * Pipeline at K step q: MFMAs on (A(q), Wq(q)), interleaved one MFMA to
 //     two VALU instructions with producing Wq(q+1) from raw W(q+1); store raw
@@ -61,7 +63,7 @@
 
 namespace awq {
 
-template <int BM, int BN, int NW>
+template <int BM, int BN, int NW, int GS>
 __global__ void __launch_bounds__(NW * 64, 1)
 k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
        const float* __restrict__ s_tab, const float* __restrict__ inv_tab,
@@ -98,8 +100,8 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
     if (threadIdx.x == 0) partials[2 * ((size_t)ai * n_tiles + T) + h] = 0.0;
     return;
   }
-  const int ngroups = K >> 7;
-  const int nk = K / KC;  // a multiple of 4
+  const int ngroups = K / (KC * GS);  // quantization groups of 32 * GS columns
+  const int nk = K / KC;               // a multiple of 4
   const float nz = neg_zero();
 
   // activation rows of this lane, as 32-bit offsets from the tile's first row
@@ -245,7 +247,7 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   // A(q+1).  Loads past the last step re-read step nk - 1 (never used), which
   // keeps the body branch-free and every wait count exact.
   GP gcur = load_params(0);
-  GP gnxt = load_params(min(1, ngroups - 1));
+  GP gnxt = load_params(min(GS == 4 ? 1 : 1 / GS, ngroups - 1));
   WR w = load_w(0);
   store_raw(0, w);
   w = load_w(1);
@@ -255,22 +257,49 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   __syncthreads();
   produce(0, gcur);
   __syncthreads();
-  for (int gi = 0; gi < ngroups; ++gi) {
-    const int q = 4 * gi;
-    a1 = load_a(q + 1);
-    step_body(a0, 0, gcur, w);  // produces Wq(q+1) from raw buffer 1
-    w = load_w(min(q + 3, nk - 1));
-    a0 = load_a(q + 2);
-    step_body(a1, 1, gcur, w);
-    w = load_w(min(q + 4, nk - 1));
-    a1 = load_a(q + 3);
-    step_body(a0, 0, gcur, w);
-    w = load_w(min(q + 5, nk - 1));
-    a0 = load_a(min(q + 4, nk - 1));
-    step_body(a1, 1, gnxt, w);  // Wq(q+4): first step of the next group
-    w = load_w(min(q + 6, nk - 1));
-    gcur = gnxt;
-    gnxt = load_params(min(gi + 2, ngroups - 1));
+  if constexpr (GS == 4) {
+    // groups of 128 columns: the parameters change every 4 steps and load a
+    // whole group ahead
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const int q = 4 * gi;
+      a1 = load_a(q + 1);
+      step_body(a0, 0, gcur, w);  // produces Wq(q+1) from raw buffer 1
+      w = load_w(min(q + 3, nk - 1));
+      a0 = load_a(q + 2);
+      step_body(a1, 1, gcur, w);
+      w = load_w(min(q + 4, nk - 1));
+      a1 = load_a(q + 3);
+      step_body(a0, 0, gcur, w);
+      w = load_w(min(q + 5, nk - 1));
+      a0 = load_a(min(q + 4, nk - 1));
+      step_body(a1, 1, gnxt, w);  // Wq(q+4): first step of the next group
+      w = load_w(min(q + 6, nk - 1));
+      gcur = gnxt;
+      gnxt = load_params(min(gi + 2, ngroups - 1));
+    }
+  } else {
+    // groups of 32 or 64 columns: step q produces Wq(q+1) with the parameters
+    // of group (q+1)/GS; two register sets roll one step ahead
+    GP ga = gnxt;  // group of step 1
+    for (int b4 = 0; b4 < nk / 4; ++b4) {
+      const int q = 4 * b4;
+      GP gb = load_params(min((q + 2) / GS, ngroups - 1));
+      a1 = load_a(q + 1);
+      step_body(a0, 0, ga, w);
+      w = load_w(min(q + 3, nk - 1));
+      a0 = load_a(q + 2);
+      ga = load_params(min((q + 3) / GS, ngroups - 1));
+      step_body(a1, 1, gb, w);
+      w = load_w(min(q + 4, nk - 1));
+      a1 = load_a(q + 3);
+      gb = load_params(min((q + 4) / GS, ngroups - 1));
+      step_body(a0, 0, ga, w);
+      w = load_w(min(q + 5, nk - 1));
+      a0 = load_a(min(q + 4, nk - 1));
+      ga = load_params(min((q + 5) / GS, ngroups - 1));
+      step_body(a1, 1, gb, w);
+      w = load_w(min(q + 6, nk - 1));
+    }
   }
 
   // epilogue: the accumulators hold X dW^T for this wavefront's tokens;
@@ -325,18 +354,18 @@ int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
   return 128;
 }
 
-template <int BM, int NW>
+template <int BM, int NW, int GS>
 static void launch_one(unsigned blocks, int unit_base, int split, hipStream_t stream,
                        const _Float16* X, const _Float16* W, const float* s_tab,
                        const float* inv_tab, const GroupParams* prm, double* partials, int N,
                        int K, int OUT, int nt, int no, int n_grid) {
-  hipLaunchKernelGGL((k_grid<BM, kGridBN, NW>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
+  hipLaunchKernelGGL((k_grid<BM, kGridBN, NW, GS>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
                      s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base, split);
 }
 
 // Blocks of the whole-tile kernel that run at once on the current device
-// (compute units x resident blocks per unit), cached per device and tile.
-template <int BM, int NW>
+// (compute units x resident blocks per unit), cached per device and kernel.
+template <int BM, int NW, int GS>
 static int64_t resident_blocks() {
   static std::mutex mu;
   static std::map<int, int64_t> cache;
@@ -347,51 +376,67 @@ static int64_t resident_blocks() {
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid<BM, kGridBN, NW>, NW * 64, 0) !=
-          hipSuccess)
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid<BM, kGridBN, NW, GS>, NW * 64,
+                                                   0) != hipSuccess)
     return 0;
   const int64_t r = (int64_t)cus * per_cu;
   cache[dev] = r;
   return r;
 }
 
-template <int BM, int NW, int HBM, int HNW>
+template <int BM, int NW, int HBM, int HNW, int GS>
 static void launch_split(int64_t units, hipStream_t stream, const _Float16* X, const _Float16* W,
                          const float* s_tab, const float* inv_tab, const GroupParams* prm,
                          double* partials, int N, int K, int OUT, int nt, int no, int n_grid) {
-  const int64_t slots = resident_blocks<BM, NW>();
+  const int64_t slots = resident_blocks<BM, NW, GS>();
   int64_t whole = units;
   if (slots > 0) {
     const int64_t rest = units % slots;
     if (units > slots && rest > 0 && rest % 8 == 0 && 2 * rest <= slots) whole = units - rest;
   }
-  launch_one<BM, NW>((unsigned)whole, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials, N, K,
-                     OUT, nt, no, n_grid);
+  launch_one<BM, NW, GS>((unsigned)whole, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials, N,
+                         K, OUT, nt, no, n_grid);
   if (whole < units)  // whole and units are multiples of 8
-    launch_one<HBM, HNW>((unsigned)(2 * (units - whole)), (int)whole, 2, stream, X, W, s_tab,
-                         inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
+    launch_one<HBM, HNW, GS>((unsigned)(2 * (units - whole)), (int)whole, 2, stream, X, W, s_tab,
+                             inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
 }
 
-void launch_grid(int tile_m, const void* X, const void* W, const float* s_tab,
+template <int GS>
+static void launch_tiles(int tile_m, int64_t units, hipStream_t stream, const _Float16* X,
+                         const _Float16* W, const float* s_tab, const float* inv_tab,
+                         const GroupParams* prm, double* partials, int N, int K, int OUT, int nt,
+                         int no, int n_grid) {
+  switch (tile_m) {
+    case 512:
+      launch_split<512, 8, 256, 8, GS>(units, stream, X, W, s_tab, inv_tab, prm, partials, N, K,
+                                       OUT, nt, no, n_grid);
+      break;
+    case 256:
+      launch_split<256, 8, 128, 4, GS>(units, stream, X, W, s_tab, inv_tab, prm, partials, N, K,
+                                       OUT, nt, no, n_grid);
+      break;
+    default:
+      launch_one<128, 4, GS>((unsigned)units, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials,
+                             N, K, OUT, nt, no, n_grid);
+      break;
+  }
+}
+
+void launch_grid(int tile_m, int group, const void* X, const void* W, const float* s_tab,
                  const float* inv_tab, const GroupParams* prm, double* partials, int64_t N,
                  int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream) {
   const int64_t units = (nt * no + 7) / 8 * 8 * n_grid;
   const _Float16* Xh = (const _Float16*)X;
   const _Float16* Wh = (const _Float16*)W;
-  switch (tile_m) {
-    case 512:
-      launch_split<512, 8, 256, 8>(units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
-                                   (int)K, (int)OUT, (int)nt, (int)no, n_grid);
-      break;
-    case 256:
-      launch_split<256, 8, 128, 4>(units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
-                                   (int)K, (int)OUT, (int)nt, (int)no, n_grid);
-      break;
-    default:
-      launch_one<128, 4>((unsigned)units, 0, 1, stream, Xh, Wh, s_tab, inv_tab, prm, partials,
-                         (int)N, (int)K, (int)OUT, (int)nt, (int)no, n_grid);
-      break;
-  }
+  if (group == 32)
+    launch_tiles<1>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
+                    (int)OUT, (int)nt, (int)no, n_grid);
+  else if (group == 64)
+    launch_tiles<2>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
+                    (int)OUT, (int)nt, (int)no, n_grid);
+  else
+    launch_tiles<4>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
+                    (int)OUT, (int)nt, (int)no, n_grid);
 }
 
 }  // namespace awq

@@ -54,9 +54,11 @@ MISALIGNED = ctypes.c_void_p(0x1004)
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(w_bit=3), _lib.AWQ_ERR_UNSUPPORTED),
-    (dict(group_size=64), _lib.AWQ_ERR_UNSUPPORTED),
-    (dict(zero_point=0), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(w_bit=2), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(w_bit=8), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(group_size=16), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(group_size=256), _lib.AWQ_ERR_UNSUPPORTED),
+    (dict(zero_point=2), _lib.AWQ_ERR_UNSUPPORTED),
     (dict(n_grid=0), _lib.AWQ_ERR_INVALID_ARG),
     (dict(n_grid=65), _lib.AWQ_ERR_INVALID_ARG),
     (dict(sal_floor=0.0), _lib.AWQ_ERR_INVALID_ARG),

@@ -381,3 +381,53 @@ def test_select_top_in_place(awq):
     t = dev(sal)
     awq.awq_select_top_channels(t, 41, out=t)
     assert np.array_equal(host(t).view(np.uint32), O.select_top_channels(sal, 41).view(np.uint32))
+
+
+# ------------------------- quantizer variants: group size, bit width, symmetric
+GPU_VARIANTS = [(64, 4, True), (32, 4, True), (128, 3, True), (64, 3, False), (128, 4, False),
+                (32, 3, False)]
+
+
+@pytest.mark.parametrize("group,w_bit,zp", GPU_VARIANTS)
+def test_variant_search_and_pack_match_oracle(awq, group, w_bit, zp):
+    _say(f"variant group {group} w_bit {w_bit} zero_point {zp}")
+    spec, X, W = synth.make_layer(2, n_tokens=300, out_features=200)
+    cfg = awq.default_config(group_size=group, w_bit=w_bit, zero_point=zp)
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    res = awq.awq_search_layer(Xd, Wd, sal, cfg)
+    ref = O.search_layer(X, W, host(sal), group=group, w_bit=w_bit, zero_point=zp)
+    losses = host(res.losses)
+    rel = np.abs(losses - ref.losses) / ref.losses
+    _say(f"  max rel loss diff {rel.max():.3e}")
+    assert np.all(rel <= LOSS_RTOL)
+    best = int(host(res.best_idx)[0])
+    check_best(best, ref.losses)
+    qw, st, zr = (host(t) for t in awq.awq_pack(Wd, res.s_best, cfg))
+    pref = O.pack(W, ref.s[best], group, w_bit, zp)
+    assert np.array_equal(qw, pref.qweight)
+    assert np.array_equal(st.view(np.uint16), pref.step16.view(np.uint16))
+    assert np.array_equal(zr.view(np.uint16), pref.zero16.view(np.uint16))
+
+
+@pytest.mark.parametrize("group,w_bit,zp", [(64, 3, True), (32, 4, False)])
+def test_variant_full_size_sampled_tiles(awq, group, w_bit, zp):
+    spec, X, W = synth.make_layer(2, 0)
+    _say(f"variant full size group {group} w_bit {w_bit} zero_point {zp}")
+    cfg = awq.default_config(group_size=group, w_bit=w_bit, zero_point=zp)
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    res = awq.awq_search_layer(Xd, Wd, sal, cfg)
+    plan = res.plan
+    nt, no = plan.n_token_tiles, plan.n_out_tiles
+    part = host(res.workspace[plan.partials_offset:plan.partials_offset + 16 * 20 * nt * no]
+                .view(torch.float64)).reshape(20, nt, no, 2).sum(axis=3)
+    s_tab, inv_s = O.scale_table(host(sal))
+    rng = np.random.default_rng(group + w_bit)
+    tm, tn = plan.tile_tokens, plan.tile_out
+    for (ti, oi) in [(nt - 1, no - 1), (0, int(rng.integers(no)))]:
+        rows = slice(ti * tm, min((ti + 1) * tm, spec.n_tokens))
+        cols = slice(oi * tn, min((oi + 1) * tn, spec.out_features))
+        for i in (0, 7, 19):
+            want = O.tile_sq_error(X, W, s_tab[i], inv_s[i], rows, cols, group, w_bit, zp)
+            assert abs(part[i, ti, oi] - want) <= LOSS_RTOL * want, (ti, oi, i)
