@@ -54,9 +54,9 @@ def stats_bytes(spec):
     return 2.0 * spec.n_tokens * spec.in_features + 4.0 * spec.in_features
 
 
-def pack_bytes(spec):
+def pack_bytes(spec, group=128):
     w = spec.out_features * spec.in_features
-    return 2.0 * w + 0.5 * w + 4.0 * w / 128 + 4.0 * spec.in_features
+    return 2.0 * w + 0.5 * w + 4.0 * w / group + 4.0 * spec.in_features
 
 
 def source_digest():
@@ -174,7 +174,8 @@ def cold_measurements(awq, cfg, layers, calib):
         ms_read = timed(lambda: calib.awq_calib_read(L["X"].data_ptr(), xb, sink.data_ptr(),
                                                      4096, stream))
         res[spec.name] = {"stats_gbs_cold": round(stats_bytes(spec) / (ms_stats * 1e-3) / 1e9, 1),
-                          "pack_gbs_cold": round(pack_bytes(spec) / (ms_pack * 1e-3) / 1e9, 1),
+                          "pack_gbs_cold": round(pack_bytes(spec, cfg.group_size) /
+                                                 (ms_pack * 1e-3) / 1e9, 1),
                           "plain_read_of_X_gbs_cold": round(xb / (ms_read * 1e-3) / 1e9, 1)}
     del flush
     out_buf = torch.empty(1024 * 512, dtype=torch.float32, device="cuda")
@@ -325,6 +326,36 @@ def ablation_bench(configs):
     return rows
 
 
+def quant_variant_bench(configs):
+    """Output MSE of plain round-to-nearest (alpha = 0) and of the searched
+    scales for each quantizer variant (group size, bit width, zero point or
+    symmetric), with the storage per weight of each format."""
+    import torch
+    import synth
+    import post_bit_weight_awq_amd as awq
+    out = []
+    for c, layer in configs:
+        spec, X, W = synth.make_layer(c, layer)
+        Xd, Wd = torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda()
+        del X, W
+        sal = awq.awq_act_stats(Xd)
+        for g in (128, 64, 32):
+            for b in (4, 3):
+                for zp in (True, False):
+                    cfg = awq.default_config(group_size=g, w_bit=b, zero_point=zp)
+                    r = awq.awq_search_layer(Xd, Wd, sal, cfg)
+                    losses = r.losses.cpu().numpy()
+                    best = int(r.best_idx.item())
+                    out.append({"config": c, "layer": spec.name, "group": g, "w_bit": b,
+                                "zero_point": zp, "rtn_loss": float(losses[0]),
+                                "awq_loss": float(losses[best]), "best_alpha": best / cfg.n_grid,
+                                "bits_per_weight": 4 + 32.0 / g})
+        log(f"quantizer variants done for {spec.name}")
+        del Xd, Wd
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of a known size (PMC byte-counter scale)."""
     import torch
@@ -348,6 +379,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
+    ap.add_argument("--group", type=int, default=128, choices=[32, 64, 128],
+                    help="quantization group size (ablation variants; the method uses 128)")
+    ap.add_argument("--w-bit", type=int, default=4, choices=[3, 4])
+    ap.add_argument("--symmetric", action="store_true",
+                    help="symmetric round-to-nearest codes instead of a zero point")
     ap.add_argument("--ablation", action="store_true",
                     help="best loss with activation vs weight saliency, all vs top 1% channels")
     ap.add_argument("--decode", action="store_true",
@@ -371,10 +407,11 @@ def main():
             sys.exit(1)
         cases = [(1, 0), (2, 0), (3, 0), (4, 0), (4, 1), (5, 0), (5, 1), (5, 2), (5, 3)]
         rows = ablation_bench(cases)
+        variants = quant_variant_bench([(2, 0), (5, 3)])
         print(json.dumps({"metric": "best search loss / round-to-nearest loss per saliency choice",
                           "unit": "ratio", "higher_is_better": False, "n_gpus": 1,
                           "data": "synthetic (seeded generators, outlier-channel activations)",
-                          "rows": rows}))
+                          "rows": rows, "quantizer_variants": variants}))
         return
 
     if args.decode:
@@ -412,7 +449,8 @@ def main():
         sys.exit(1)
     awq.load()
     cfgspec = synth.CONFIGS[args.config]
-    cfg = awq.default_config()
+    cfg = awq.default_config(group_size=args.group, w_bit=args.w_bit,
+                             zero_point=not args.symmetric)
     layers = []
     for li, spec in enumerate(cfgspec.layers):
         _, X, W = synth.make_layer(args.config, li)
@@ -430,8 +468,8 @@ def main():
                  best=torch.empty(1, dtype=torch.int32, device="cuda"),
                  s_best=torch.empty(k, dtype=torch.float32, device="cuda"),
                  qw=torch.empty((o, k // 8), dtype=torch.int32, device="cuda"),
-                 st=torch.empty((o, k // 128), dtype=torch.float16, device="cuda"),
-                 zr=torch.empty((o, k // 128), dtype=torch.float16, device="cuda"))
+                 st=torch.empty((o, k // cfg.group_size), dtype=torch.float16, device="cuda"),
+                 zr=torch.empty((o, k // cfg.group_size), dtype=torch.float16, device="cuda"))
         layers.append(L)
         log(f"layer {spec.name}: {n}x{k}->{o}")
     torch.cuda.synchronize()
@@ -493,7 +531,7 @@ def main():
             "search_tflops": round(F[li] / ((per["prepare"][li] + per["grid"][li] +
                                              per["select"][li]) * 1e-3) / 1e12, 2),
             "stats_gbs": round(stats_bytes(spec) / (per["stats"][li] * 1e-3) / 1e9, 1),
-            "pack_gbs": round(pack_bytes(spec) / (per["pack"][li] * 1e-3) / 1e9, 1),
+            "pack_gbs": round(pack_bytes(spec, cfg.group_size) / (per["pack"][li] * 1e-3) / 1e9, 1),
         }
     traffic = traffic_from_profiles(cfgspec.workload)
     calib = load_calib()
@@ -521,7 +559,8 @@ def main():
         "config": {"workload": cfgspec.workload, "layers": [
             {"name": L["spec"].name, "n_tokens": L["spec"].n_tokens,
              "in_features": L["spec"].in_features, "out_features": L["spec"].out_features}
-            for L in layers], "group_size": 128, "w_bit": 4, "n_grid": cfg.n_grid},
+            for L in layers], "group_size": cfg.group_size, "w_bit": cfg.w_bit,
+            "zero_point": bool(cfg.zero_point), "n_grid": cfg.n_grid},
         "roofline": {"bound": "mfma",
                      "kernel": "k_grid (fused alpha-grid search; per search: the whole-tile "
                                "launch plus, when the last round is partly filled, the "
