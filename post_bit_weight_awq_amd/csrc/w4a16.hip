@@ -100,12 +100,178 @@ k_w4a16(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// Up to MT (1, 2 or 4) tokens: a streaming product without MFMA.  Each block
+// first copies the activations into LDS, each group of 8 reordered as
+// (x0, x4), (x1, x5), (x2, x6), (x3, x7) to match the code pairs the bit
+// placement yields, together with the sum of every 32-column slice.  Then
+// each wavefront takes whole output rows, two at a time: lane l reads the
+// 32-code slices l, l + 64, ... of both rows with all their 16-byte loads in
+// flight, forms sum_k x q over each slice with v_dot2_f32_f16 (exact fp16
+// products, binary32 sums), adds step * (that - zero * slice sum), and the
+// wavefront adds its lanes at the end of the row pair.
+constexpr int kGemvThreads = 512;
+
+// SL: 16-byte loads per lane per row (K <= 64 * SL * 32); RW rows per pass.
+template <int MT, int SL, int RW>
+__global__ void __launch_bounds__(kGemvThreads)
+k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __restrict__ qw,
+             const _Float16* __restrict__ step16, const _Float16* __restrict__ zero16,
+             float* __restrict__ Y) {
+  extern __shared__ uint4 lds[];  // MT x (K / 8) reordered activation octets, then slice sums
+  const int n8 = K >> 3, ns = K >> 5, ng = K >> 7;
+  float* xsum = (float*)(lds + MT * n8);  // [MT][ns]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int waves = gridDim.x * (kGemvThreads / 64);
+  for (int e = tid; e < MT * n8; e += kGemvThreads) {
+    const int t = e / n8, c = e - t * n8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t < M) v = *(const uint4*)(X + (size_t)t * K + 8 * c);
+    lds[e] = make_uint4(lo_lo(v.x, v.z), hi_hi(v.x, v.z), lo_lo(v.y, v.w), hi_hi(v.y, v.w));
+  }
+  __syncthreads();
+  for (int e = tid; e < MT * ns; e += kGemvThreads) {
+    const int t = e / ns, c = e - t * ns;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = lds[t * n8 + 4 * c + j];
+      s += f16_lo(v.x) + f16_hi(v.x) + f16_lo(v.y) + f16_hi(v.y) + f16_lo(v.z) + f16_hi(v.z) +
+           f16_lo(v.w) + f16_hi(v.w);
+    }
+    xsum[e] = s;
+  }
+  __syncthreads();
+  constexpr uint32_t kBias = 0x64006400u;
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  for (int ob = blockIdx.x * (kGemvThreads / 64) + wave; ob < OUT; ob += RW * waves) {
+    int orow[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) orow[r] = min(ob + r * waves, OUT - 1);  // past the end: repeat
+    // the pass's codes, steps and zeros are all requested before any is used
+    uint4 cw[RW][SL];
+    _Float16 sb[RW][SL], zb[RW][SL];
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      if (64 * i >= ns) break;  // wavefront-uniform
+      const int c = min(lane + 64 * i, ns - 1);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        cw[r][i] = qw[(size_t)orow[r] * ns + c];
+        sb[r][i] = step16[(size_t)orow[r] * ng + (c >> 2)];
+        zb[r][i] = zero16[(size_t)orow[r] * ng + (c >> 2)];
+      }
+    }
+    float y[RW][MT];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) y[r][t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int c = lane + 64 * i;
+      if (64 * i >= ns) break;  // wavefront-uniform
+      if (c < ns) {
+        uint4 xv[MT][4];
+        float xs[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xv[t][j] = lds[t * n8 + 4 * c + j];
+          xs[t] = xsum[t * ns + c];
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          const float st = (float)sb[r][i];
+          const float zr = (float)zb[r][i];
+          const uint32_t w[4] = {cw[r][i].x, cw[r][i].y, cw[r][i].z, cw[r][i].w};
+          float d[MT];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) d[t] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            uint32_t p[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) p[h] = sub_f16x2(((w[j] >> (4 * h)) & 0x000F000Fu) | kBias, kBias);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+              const uint32_t xp[4] = {xv[t][j].x, xv[t][j].y, xv[t][j].z, xv[t][j].w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h)
+                d[t] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, p[h]),
+                                              __builtin_bit_cast(half2v, xp[h]), d[t], false);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < MT; ++t) y[r][t] = fmaf(st, fmaf(-zr, xs[t], d[t]), y[r][t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) y[r][t] += __shfl_xor(y[r][t], d, 64);
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        if (ob + r * waves < OUT) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+            if (t < M) Y[(size_t)t * OUT + ob + r * waves] = y[r][t];
+        }
+      }
+    }
+  }
+}
+
+template <int MT, int SL, int RW>
+static void launch_gemv(const _Float16* X, int M, int K, int OUT, const uint4* qw,
+                        const _Float16* st, const _Float16* zr, float* Y, hipStream_t stream) {
+  const size_t lds = (size_t)MT * (K / 8) * 16 + (size_t)MT * (K / 32) * 4;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const int rows_per_block = RW * (kGemvThreads / 64);
+  const int want = (OUT + rows_per_block - 1) / rows_per_block;
+  const int blocks = want < 2 * cus ? want : 2 * cus;
+  hipLaunchKernelGGL((k_w4a16_gemv<MT, SL, RW>), dim3(blocks), dim3(kGemvThreads), lds, stream, X,
+                     M, K, OUT, qw, st, zr, Y);
+}
+
+template <int MT>
+static void launch_gemv_k(const _Float16* X, int M, int K, int OUT, const uint4* qw,
+                          const _Float16* st, const _Float16* zr, float* Y, hipStream_t stream) {
+  if (K <= 64 * 4 * 32)
+    launch_gemv<MT, 4, 4>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else
+    launch_gemv<MT, 8, 2>(X, M, K, OUT, qw, st, zr, Y, stream);
+}
+
 hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const int32_t* qweight,
                         const void* step16, const void* zero16, float* Y, hipStream_t stream) {
+  const _Float16* Xh = (const _Float16*)X;
+  const uint4* qw = (const uint4*)qweight;
+  const _Float16* st = (const _Float16*)step16;
+  const _Float16* zr = (const _Float16*)zero16;
+  // the streaming kernel keeps a row's codes in registers (K <= 16384) and the
+  // activations in LDS (at most 64 KiB)
+  const bool gemv_fits = K <= 64 * 8 * 32 && M <= 4 && (size_t)M * K * 2 <= 65536;
+  if (gemv_fits) {
+    if (M == 1)
+      launch_gemv_k<1>(Xh, (int)M, (int)K, (int)OUT, qw, st, zr, Y, stream);
+    else if (M == 2)
+      launch_gemv_k<2>(Xh, (int)M, (int)K, (int)OUT, qw, st, zr, Y, stream);
+    else
+      launch_gemv_k<4>(Xh, (int)M, (int)K, (int)OUT, qw, st, zr, Y, stream);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((OUT + 15) / 16), (unsigned)((M + 15) / 16));
-  hipLaunchKernelGGL(k_w4a16, grid, dim3(kW4Slices * 64), 0, stream, (const _Float16*)X, (int)M,
-                     (int)K, (int)OUT, (const uint4*)qweight, (const _Float16*)step16,
-                     (const _Float16*)zero16, Y);
+  hipLaunchKernelGGL(k_w4a16, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K, (int)OUT,
+                     qw, st, zr, Y);
   return hipGetLastError();
 }
 
