@@ -509,11 +509,14 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     per = {nm: [0.0] * len(layers) for nm in names}
+    samples = {nm: [[] for _ in layers] for nm in names}
     for s in range(args.steps):
         for li in range(len(layers)):
             e = evs[s][li]
             for j, nm in enumerate(names):
-                per[nm][li] += e[j].elapsed_time(e[j + 1]) / args.steps
+                dt = e[j].elapsed_time(e[j + 1])
+                per[nm][li] += dt / args.steps
+                samples[nm][li].append(dt)
 
     F = [search_flops(L["spec"], cfg.n_grid) for L in layers]
     total_F = sum(F)
@@ -527,6 +530,9 @@ def main():
             "shape": [spec.n_tokens, spec.in_features, spec.out_features],
             "best_idx": int(L["best"].item()),
             "ms": {nm: round(per[nm][li], 5) for nm in names},
+            "ms_median": {nm: round(sorted(samples[nm][li])[len(samples[nm][li]) // 2], 5)
+                          for nm in names},
+            "ms_min": {nm: round(min(samples[nm][li]), 5) for nm in names},
             "grid_tflops": round(F[li] / (per["grid"][li] * 1e-3) / 1e12, 2),
             "search_tflops": round(F[li] / ((per["prepare"][li] + per["grid"][li] +
                                              per["select"][li]) * 1e-3) / 1e12, 2),
