@@ -56,7 +56,13 @@ typedef enum awq_status {
   AWQ_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment       */
   AWQ_ERR_UNSUPPORTED = -2, /* configuration outside what is implemented  */
   AWQ_ERR_WORKSPACE = -3,   /* workspace smaller than the queried size    */
-  AWQ_ERR_HIP = -4          /* the HIP runtime reported an error          */
+  AWQ_ERR_HIP = -4,         /* the HIP runtime reported an error          */
+  AWQ_ERR_NONFINITE = -5    /* no grid point gave a finite loss: never
+                               returned by a call (the search runs
+                               asynchronously); it names the outcome that
+                               best_idx_out = -1 reports after the stream
+                               sync, as the search_scale listing keeps no
+                               scale when no loss beats infinity          */
 } awq_status;
 
 /* Quantization settings (the quant_config of the dev.to page's "What do you

@@ -112,6 +112,14 @@ class SearchResult:
     workspace: torch.Tensor  # uint8 workspace (tile partial sums, scale table, group parameters)
     plan: AwqSearchPlan
 
+    def best(self) -> int:
+        """The chosen grid index after synchronizing with the search's stream;
+        raises AwqError(AWQ_ERR_NONFINITE) when no loss was finite."""
+        b = int(self.best_idx.item())
+        if b < 0:
+            raise AwqError(_lib.AWQ_ERR_NONFINITE, "no grid point gave a finite loss")
+        return b
+
 
 def awq_search_layer(X: torch.Tensor, W: torch.Tensor, sal: torch.Tensor,
                      cfg: Optional[AwqConfig] = None, *, workspace: Optional[torch.Tensor] = None,

@@ -13,9 +13,10 @@ AWQ_ERR_INVALID_ARG = -1
 AWQ_ERR_UNSUPPORTED = -2
 AWQ_ERR_WORKSPACE = -3
 AWQ_ERR_HIP = -4
+AWQ_ERR_NONFINITE = -5
 STAGE_PREPARE, STAGE_GRID, STAGE_SELECT, STAGE_ALL = 1, 2, 4, 7
 STATUS_NAMES = {0: "AWQ_OK", -1: "AWQ_ERR_INVALID_ARG", -2: "AWQ_ERR_UNSUPPORTED",
-                -3: "AWQ_ERR_WORKSPACE", -4: "AWQ_ERR_HIP"}
+                -3: "AWQ_ERR_WORKSPACE", -4: "AWQ_ERR_HIP", -5: "AWQ_ERR_NONFINITE"}
 
 #: every symbol the header declares
 EXPORTS = (

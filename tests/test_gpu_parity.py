@@ -234,6 +234,9 @@ def test_search_degenerate_inputs(awq):
     _, _, sal, res = run_layer(awq, np.ones((4, 256), np.float16), Wn)
     assert int(host(res.best_idx)[0]) == -1
     assert np.all(np.isnan(host(res.s_best)))
+    with pytest.raises(awq.AwqError) as err:
+        res.best()
+    assert err.value.code == awq._lib.AWQ_ERR_NONFINITE
 
 
 # ------------------------------------------- full-size layers, tile sampled
