@@ -622,3 +622,25 @@ def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
         monkeypatch.setattr(O, "quantize", negz)
         with pytest.raises(AssertionError):
             test_zero_range_group()
+
+
+# ------------------------------------------------------ regression fixtures
+def test_input_generator_manifest():
+    """The seeded inputs are frozen: every configured layer's leading cut hashes
+    to the recorded digest (tests/golden/make_golden.py wrote them)."""
+    g = json.load(open(os.path.join(GOLD, "input_manifest.json")))
+    for key, cfg in synth.CONFIGS.items():
+        for li, spec in enumerate(cfg.layers):
+            _, X, W = synth.make_layer(key, li, **g["cut"])
+            assert synth.digest(X, W) == g["digests"][f"{key}:{spec.name}"], (key, spec.name)
+
+
+def test_oracle_config1_regression():
+    g = json.load(open(os.path.join(GOLD, "oracle_config1.json")))
+    _, X, W = synth.make_layer(1, 0)
+    sal = O.act_stats(X)
+    assert synth.digest(sal) == g["sal_digest"]
+    res = O.search_layer(X, W, sal)
+    # binary64 contractions: equal up to the BLAS's summation order
+    assert res.losses == pytest.approx(np.array(g["losses"]), rel=1e-12, abs=0)
+    assert res.best == g["best"]
