@@ -66,6 +66,20 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
+def grid_kernel_names(layers, cfg):
+    """Names of the grid-stage kernels the searches launch: the ping-pong
+    kernel for groups of 128 columns on 512- and 256-token tiles, else k_grid."""
+    import post_bit_weight_awq_amd as P
+    names = []
+    for L in layers:
+        sp = L["spec"]
+        plan = P.awq_search_plan(sp.n_tokens, sp.in_features, sp.out_features, cfg)
+        nm = "k_grid_pp" if cfg.group_size == 128 and plan.tile_tokens in (512, 256) else "k_grid"
+        if nm not in names:
+            names.append(nm)
+    return " + ".join(names)
+
+
 def traffic_from_profiles(workload):
     """HBM bytes per launch of the grid kernel from the committed PMC summary,
     or None when there is none or the kernel source changed since."""
@@ -568,9 +582,9 @@ def main():
             for L in layers], "group_size": cfg.group_size, "w_bit": cfg.w_bit,
             "zero_point": bool(cfg.zero_point), "n_grid": cfg.n_grid},
         "roofline": {"bound": "mfma",
-                     "kernel": "k_grid (fused alpha-grid search; per search: the whole-tile "
-                               "launch plus, when the last round is partly filled, the "
-                               "half-tile launch)",
+                     "kernel": grid_kernel_names(layers, cfg) + " (fused alpha-grid search; "
+                               "per search: the whole-tile launch plus, when the last round "
+                               "is partly filled, the half-tile launch)",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": traffic,

@@ -13,6 +13,11 @@
 // of dW has relative size <= 2^-11 and zero mean; it changes a loss by a
 // second-order amount (measured ~1e-6 relative).
 //
+// Two kernels share this file.  k_grid_pp (after k_grid) runs groups of 128
+// columns on the 512- and 256-token tiles; k_grid runs groups of 32 and 64
+// columns and the 128-token tile.  The notes below describe k_grid; those of
+// k_grid_pp stand above it.
+//
 // Layout (BM tokens x BN outputs per block, NW wavefronts, K steps of 32):
 //   * NW wavefronts stacked along tokens (8 for the 512- and 256-token tiles,
 //     two per SIMD, so one wavefront's loads and weight production overlap the
@@ -342,6 +347,332 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   }
 }
 
+// Grid kernel for groups of 128 columns (the 512- and 256-token tiles):
+// ping-pong phases, operands staged in LDS by whole-line direct loads.
+//
+// Loads in the MFMA fragment shape (16 rows x 64 bytes per instruction) touch
+// half of 16 cache lines each, and the vector memory path moves them at less
+// than half the rate of loads that cover whole 128-byte lines (measured on
+// this chip: ~21 against ~46 bytes per clock per compute unit from L2).  So
+// activations and raw weights move in chunks of 64 columns (two K steps):
+// each direct-to-LDS load covers 8 rows x 128 bytes, 16-byte piece p of row r
+// stored at position p ^ (r & 7), which keeps the fragment reads and the
+// producers' row-per-lane reads free of bank conflicts.
+//
+// The eight wavefronts form two groups of four (one wavefront per SIMD in
+// each).  Every K step has two phases separated by block barriers.  In each
+// phase one group multiplies and the other prepares, so on every SIMD one
+// wavefront's MFMAs run beside the other wavefront's VALU and LDS work:
+//   * preparing step r: produce the group's 64 rows of dW(r+1) (each
+//     wavefront one 8-column piece), read step r's B fragments and, for even
+//     r, its A fragments into registers;
+//   * multiplying step r: the MFMAs, and between their two halves the loads:
+//     for even r it first reads step r+1's A fragments and then refills its
+//     activation buffer with the next chunk; its weight load; its group's
+//     data for a later column group.
+// Group 0 prepares step r in phase 2r-1 and multiplies it in phase 2r;
+// group 1 prepares it in phase 2r and multiplies it in phase 2r+1.  dW(j) is
+// complete after phase 2j-2 and first read in phase 2j-1 (two dW buffers).
+//
+// Loads, each by the wavefront or group that uses the data:
+//   * activations: a wavefront's own 64 rows, one buffer per wavefront,
+//     refilled once both steps of its chunk have their fragments in registers;
+//   * raw weights: a group's own 64 rows, ring of three chunks, each chunk
+//     issued four to five steps before its first use;
+//   * per-group parameters and scales: a group's own copy, two column groups
+//     in flight.
+// The loads are inline assembly, so the compiler does not wait for them
+// before every LDS read; at the end of each multiply phase a wavefront waits
+// for all of its loads except that phase's own.  Nothing else in the loop
+// uses the vector memory counter, which keeps those counts exact.
+template <int BM, int BN>
+__global__ void __launch_bounds__(512, 1)
+k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
+          const float* __restrict__ s_tab, const float* __restrict__ inv_tab,
+          const GroupParams* __restrict__ prm, double* __restrict__ partials, int N, int K,
+          int OUT, int n_t_tiles, int n_o_tiles, int n_grid, int unit_base, int split) {
+  constexpr int NW = 8;
+  constexpr int KC = 32;            // k per MFMA step
+  constexpr int KCH = 64;           // k per load chunk
+  constexpr int GC = 128;           // columns per quantization group
+  constexpr int WMT = BM / NW;      // tokens per wavefront
+  constexpr int MBW = WMT / 16;
+  constexpr int NBW = BN / 16;
+  constexpr int LDW = KC + 8;       // dW row stride (halves)
+  constexpr int ALD = WMT / 8;      // activation loads per wavefront and chunk
+  static_assert(BN == 128 && MBW >= 1 && ALD >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) _Float16 wq0[BN * LDW];
+  __shared__ __attribute__((aligned(16))) _Float16 wq1[BN * LDW];
+  __shared__ __attribute__((aligned(16))) _Float16 abuf[NW][WMT * KCH];  // per wavefront
+  __shared__ __attribute__((aligned(16))) _Float16 wraw[3][BN * KCH];    // ring of chunks
+  __shared__ __attribute__((aligned(16))) float4 gprm[2][2][64];         // [slot][group][row]
+  __shared__ __attribute__((aligned(16))) float gscl[2][2][2 * GC];      // [slot][group] s | 1/s
+  __shared__ double red[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n_tiles = n_t_tiles * n_o_tiles;
+  const int b = blockIdx.x;
+  const int u = unit_base + (split == 1 ? b : (b & 7) + 8 * (b >> 4));
+  const int h = split == 1 ? 0 : (b >> 3) & 1;
+  const int jb = u >> 3;
+  const int ai = jb % n_grid;
+  const int T = (jb / n_grid) * 8 + (u & 7);
+  if (T >= n_tiles) return;
+  const int tt = T / n_o_tiles, ot = T - tt * n_o_tiles;
+  const int t0 = tt * BM * split + h * BM, o0 = ot * BN;
+  if (t0 >= N) {
+    if (threadIdx.x == 0) partials[2 * ((size_t)ai * n_tiles + T) + h] = 0.0;
+    return;
+  }
+  const int ngroups = K / GC;
+  const int nk = K / KC;     // a multiple of 4
+  const int nch = K / KCH;   // chunks
+  const float nz = neg_zero();
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wv >> 2;   // 0: multiplies first; 1: prepares first
+  const int pc = wv & 3;     // the wavefront's 8-column piece of a step in production
+  const int prow = 64 * grp + lane;
+
+  // whole-line loads: lane l covers row l/8 of the load's 8 rows and stores
+  // its 16 bytes at position l%8, i.e. it reads piece (l%8) ^ (row & 7)
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const _Float16* xt = X + (size_t)t0 * K;
+  uint32_t pa[ALD];  // byte offsets from xt of this lane's pieces (chunk 0)
+#pragma unroll
+  for (int i = 0; i < ALD; ++i) {
+    const int r = 8 * i + lrow;  // row within the wavefront's rows
+    const int row = min(t0 + wave * WMT + r, N - 1) - t0;
+    pa[i] = 2u * ((uint32_t)row * (uint32_t)K + 8 * (lpos ^ (r & 7)));
+  }
+  const _Float16* wt = W + (size_t)o0 * K;
+  uint32_t pw[2];  // this wavefront's two weight loads per chunk: group rows 16pc + 8i ..
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 64 * grp + 16 * pc + 8 * i + lrow;
+    const int go = min(o0 + r, OUT - 1) - o0;
+    pw[i] = 2u * ((uint32_t)go * (uint32_t)K + 8 * (lpos ^ (r & 7)));
+  }
+  // per-group loads of the wavefront's group: wavefront 0 of the group the
+  // parameters of its 64 rows, wavefront 1 the scales (lanes 0-31) and the
+  // reciprocals (lanes 32-63, reached from the scale table's base: the
+  // library places that table a short positive distance after the scales)
+  const GroupParams* pgp = prm + (size_t)ai * ngroups * OUT;
+  const uint32_t pgo = 16u * (uint32_t)min(o0 + 64 * grp + lane, OUT - 1);
+  const float* pgs = s_tab + (size_t)ai * K;
+  const uint32_t pso = 16 * (lane & 31) +
+                       (lane < 32 ? 0u : (uint32_t)((const char*)inv_tab - (const char*)s_tab));
+
+  floatx4 acc[MBW][NBW];
+#pragma unroll
+  for (int m = 0; m < MBW; ++m)
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) acc[m][n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // global address = uniform base + per-lane 32-bit byte offset
+  auto dma = [&](const void* base, uint32_t off, const void* l) {
+    const uint32_t la = (uint32_t)(uintptr_t)l;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(la)
+                 : "memory", "m0");
+  };
+  // Loads past the last chunk or group re-read the last one (never used)
+  // into the slot the unclamped index selects, so the load counts never vary.
+  auto dma_a = [&](int ch) {
+    const _Float16* base = xt + min(ch, nch - 1) * KCH;
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) dma(base, pa[i], &abuf[wv][8 * i * KCH]);
+  };
+  auto dma_w = [&](int ch, int i) {
+    dma(wt + min(ch, nch - 1) * KCH, pw[i], &wraw[ch % 3][(64 * grp + 16 * pc + 8 * i) * KCH]);
+  };
+  auto dma_g = [&](int g) {
+    const int src = min(g, ngroups - 1);
+    if (pc == 0)
+      dma(pgp + (size_t)src * OUT, pgo, &gprm[g & 1][grp][0]);
+    else if (pc == 1)
+      dma(pgs + src * GC, pso, &gscl[g & 1][grp][0]);
+  };
+  // this wavefront's part of dW(step): piece pc of row prow.  Split in two so
+  // that its LDS reads can be issued before other reads and its arithmetic
+  // run while those land.
+  struct PIn {
+    float4 s0, s1, i0, i1, gp;
+    uint4 r;
+  };
+  auto produce_in = [&](int step) {
+    PIn p;
+    const int gs = (step >> 2) & 1, c = 8 * (step & 3) + 2 * pc;  // scale index / 4
+    const float4* sc = (const float4*)&gscl[gs][grp][0];
+    p.s0 = sc[c];
+    p.s1 = sc[c + 1];
+    p.i0 = sc[GC / 4 + c];
+    p.i1 = sc[GC / 4 + c + 1];
+    const int piece = 4 * (step & 1) + pc;
+    p.r = *(const uint4*)(&wraw[(step >> 1) % 3][prow * KCH + 8 * (piece ^ (prow & 7))]);
+    p.gp = gprm[gs][grp][lane];  // step, 1/step, -zero, 15 - zero
+    return p;
+  };
+  auto produce_out = [&](const PIn& p, _Float16* dst) {
+    const float sv[8] = {p.s0.x, p.s0.y, p.s0.z, p.s0.w, p.s1.x, p.s1.y, p.s1.z, p.s1.w};
+    const float iv[8] = {p.i0.x, p.i0.y, p.i0.z, p.i0.w, p.i1.x, p.i1.y, p.i1.z, p.i1.w};
+    const uint32_t w[4] = {p.r.x, p.r.y, p.r.z, p.r.w};
+    const float4 gp = p.gp;
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float fa = mul_f16_f32<false>(w[e], sv[2 * e], nz);
+      const float fb = mul_f16_f32<true>(w[e], sv[2 * e + 1], nz);
+      const float ca = med3(rintf(fa * gp.y), gp.z, gp.w) * gp.x;
+      const float cb = med3(rintf(fb * gp.y), gp.z, gp.w) * gp.x;
+      const uint32_t wq2 = mul_f32_to_f16x2(ca, iv[2 * e], cb, iv[2 * e + 1], nz);
+      o[e] = sub_f16x2(wq2, w[e]);
+    }
+    *(uint4*)(&dst[prow * LDW + 8 * pc]) = make_uint4(o[0], o[1], o[2], o[3]);
+  };
+  auto produce = [&](int step, _Float16* dst) { produce_out(produce_in(step), dst); };
+
+  // operands of the next multiply phase: A of both steps of a chunk, B of one step
+  half8 a0[MBW], a1[MBW], bv[NBW];
+  auto read_a = [&](half8 (&av)[MBW], int s) {
+#pragma unroll
+    for (int m = 0; m < MBW; ++m) {
+      const int r = 16 * m + (lane & 15);
+      const int piece = 4 * s + (lane >> 4);
+      av[m] = *(const half8*)(&abuf[wv][r * KCH + 8 * (piece ^ (r & 7))]);
+    }
+  };
+  auto read_b = [&](const _Float16* src) {
+#pragma unroll
+    for (int n = 0; n < NBW; ++n)
+      bv[n] = *(const half8*)(&src[(n * 16 + (lane & 15)) * LDW + 8 * (lane >> 4)]);
+  };
+  auto mfma_rows = [&](const half8 (&av)[MBW], int m0, int m1) {
+#pragma unroll
+    for (int m = m0; m < m1; ++m)
+#pragma unroll
+      for (int n = 0; n < NBW; ++n)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[m], bv[n], acc[m][n], 0, 0, 0);
+  };
+  // multiply phase of step r (s = r % 2) on A fragments av.  The multiplying
+  // wavefront also issues the loads: for s == 0 it first reads step r+1's A
+  // fragments, then refills its activation buffer with chunk r/2 + 1; its
+  // weight load for chunk (r+5)/2; for r % 4 == 1 its group's data for column
+  // group (r+3)/4.
+  auto multiply = [&](const half8 (&av)[MBW], int r, int s) {
+    if (s == 0) read_a(a1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(av, 0, MBW / 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s == 0) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): A(r+1) read before the refill
+      dma_a(r / 2 + 1);
+    }
+    dma_w((r + 5) >> 1, (r + 1) & 1);
+    if ((r & 3) == 1) dma_g((r + 3) / 4);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(av, MBW / 2, MBW);
+  };
+  // preparation of step r: this wavefront's part of dW(r+1) into `nxt`, the B
+  // fragments of step r (dW(r) in `cur`) and for s == 0 its A fragments
+  auto prepare = [&](int r, int s, const _Float16* cur, _Float16* nxt) {
+    const PIn p = produce_in(r + 1);
+    read_b(cur);
+    if (s == 0) read_a(a0, 0);
+    produce_out(p, nxt);
+  };
+  // after a multiply phase: all loads but that phase's own (for s == 0 the
+  // activation chunk and a weight load, else a weight load and possibly the
+  // group data) have landed
+  auto end_phase = [&](int wait_keep) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (wait_keep == 1) __builtin_amdgcn_s_waitcnt(0x0f71);
+    if (wait_keep == 1 + ALD) __builtin_amdgcn_s_waitcnt(0x0f70 | (1 + ALD));
+    __syncthreads();
+  };
+
+  // prologue: group data 0, activation chunk 0, weight chunks 0..2 of the
+  // group's rows; all of dW(0)
+  dma_g(0);
+  dma_a(0);
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    dma_w(c, 0);
+    dma_w(c, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  __syncthreads();
+  produce(0, wq0);
+  __syncthreads();
+  // The two groups run separate loops (a wave-uniform branch), so the
+  // fragment registers written by a preparation are the ones the next
+  // multiply phase reads; both loops pass the same barriers.
+  if (grp == 0) {
+    prepare(0, 0, wq0, wq1);  // phase -1
+    end_phase(0);
+    for (int k = 0; k < nk; k += 2) {
+      multiply(a0, k, 0);           // phase 2k: step k
+      end_phase(1 + ALD);
+      prepare(k + 1, 1, wq1, wq0);  // phase 2k+1
+      end_phase(0);
+      multiply(a1, k + 1, 1);       // phase 2k+2: step k+1
+      end_phase(1);
+      prepare(k + 2, 0, wq0, wq1);  // phase 2k+3
+      end_phase(0);
+    }
+  } else {
+    end_phase(0);  // phase -1
+    for (int k = 0; k < nk; k += 2) {
+      prepare(k, 0, wq0, wq1);      // phase 2k
+      end_phase(0);
+      multiply(a0, k, 0);           // phase 2k+1: step k
+      end_phase(1 + ALD);
+      prepare(k + 1, 1, wq1, wq0);  // phase 2k+2
+      end_phase(0);
+      multiply(a1, k + 1, 1);       // phase 2k+3: step k+1
+      end_phase(1);
+    }
+  }
+  // the last loads (re-reads, never used) land before the block ends
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+
+  const int tb = t0 + wave * WMT + 4 * (lane >> 4);
+  const int oc = o0 + (lane & 15);
+  const bool full = (t0 + BM <= N) && (o0 + BN <= OUT);
+  double dsum = 0.0;
+#pragma unroll
+  for (int m = 0; m < MBW; ++m) {
+    float sq = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) {
+      const int o = oc + n * 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tb + m * 16 + r;
+        const float d = acc[m][n][r];
+        if (full || (t < N && o < OUT)) sq = fmaf(d, d, sq);
+      }
+    }
+    dsum += (double)sq;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) dsum += __shfl_xor(dsum, d, kWave);
+  if (lane == 0) red[wave] = dsum;
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += red[w];
+    double* slot = partials + 2 * ((size_t)ai * n_tiles + T);
+    if (split == 1) {
+      slot[0] = tot;
+      slot[1] = 0.0;
+    } else {
+      slot[h] = tot;
+    }
+  }
+}
+
 int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
   // Largest token tile whose block count still fills the chip a few times
   // over; larger tiles spread the weight producer over more tokens and read
@@ -354,11 +685,27 @@ int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
   return 128;
 }
 
+// The ping-pong kernel takes groups of 128 columns on the 8-wavefront tiles
+// when the reciprocal table lies a short positive distance after the scale
+// table (it reaches both through one base address); otherwise k_grid runs.
+template <int NW, int GS>
+static constexpr bool pp_shape() {
+  return GS == 4 && NW == 8;
+}
+
 template <int BM, int NW, int GS>
-static void launch_one(unsigned blocks, int unit_base, int split, hipStream_t stream,
+static void launch_one(bool pp, unsigned blocks, int unit_base, int split, hipStream_t stream,
                        const _Float16* X, const _Float16* W, const float* s_tab,
                        const float* inv_tab, const GroupParams* prm, double* partials, int N,
                        int K, int OUT, int nt, int no, int n_grid) {
+  if constexpr (pp_shape<NW, GS>()) {
+    if (pp) {
+      hipLaunchKernelGGL((k_grid_pp<BM, kGridBN>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
+                         s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base,
+                         split);
+      return;
+    }
+  }
   hipLaunchKernelGGL((k_grid<BM, kGridBN, NW, GS>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
                      s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base, split);
 }
@@ -366,58 +713,67 @@ static void launch_one(unsigned blocks, int unit_base, int split, hipStream_t st
 // Blocks of the whole-tile kernel that run at once on the current device
 // (compute units x resident blocks per unit), cached per device and kernel.
 template <int BM, int NW, int GS>
-static int64_t resident_blocks() {
+static int64_t resident_blocks(bool pp) {
   static std::mutex mu;
-  static std::map<int, int64_t> cache;
+  static std::map<int, int64_t> cache;  // key: 2 * device + pp
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  pp = pp && pp_shape<NW, GS>();
+  const int key = 2 * dev + (pp ? 1 : 0);
   std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(dev);
+  auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid<BM, kGridBN, NW, GS>, NW * 64,
-                                                   0) != hipSuccess)
-    return 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) {
+    if (pp)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid_pp<BM, kGridBN>, NW * 64,
+                                                       0);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid<BM, kGridBN, NW, GS>,
+                                                       NW * 64, 0);
+  }
+  if (e != hipSuccess) return 0;
   const int64_t r = (int64_t)cus * per_cu;
-  cache[dev] = r;
+  cache[key] = r;
   return r;
 }
 
 template <int BM, int NW, int HBM, int HNW, int GS>
-static void launch_split(int64_t units, hipStream_t stream, const _Float16* X, const _Float16* W,
-                         const float* s_tab, const float* inv_tab, const GroupParams* prm,
-                         double* partials, int N, int K, int OUT, int nt, int no, int n_grid) {
-  const int64_t slots = resident_blocks<BM, NW, GS>();
+static void launch_split(bool pp, int64_t units, hipStream_t stream, const _Float16* X,
+                         const _Float16* W, const float* s_tab, const float* inv_tab,
+                         const GroupParams* prm, double* partials, int N, int K, int OUT, int nt,
+                         int no, int n_grid) {
+  const int64_t slots = resident_blocks<BM, NW, GS>(pp);
   int64_t whole = units;
   if (slots > 0) {
     const int64_t rest = units % slots;
     if (units > slots && rest > 0 && rest % 8 == 0 && 2 * rest <= slots) whole = units - rest;
   }
-  launch_one<BM, NW, GS>((unsigned)whole, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials, N,
-                         K, OUT, nt, no, n_grid);
+  launch_one<BM, NW, GS>(pp, (unsigned)whole, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials,
+                         N, K, OUT, nt, no, n_grid);
   if (whole < units)  // whole and units are multiples of 8
-    launch_one<HBM, HNW, GS>((unsigned)(2 * (units - whole)), (int)whole, 2, stream, X, W, s_tab,
-                             inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
+    launch_one<HBM, HNW, GS>(pp, (unsigned)(2 * (units - whole)), (int)whole, 2, stream, X, W,
+                             s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
 }
 
 template <int GS>
-static void launch_tiles(int tile_m, int64_t units, hipStream_t stream, const _Float16* X,
-                         const _Float16* W, const float* s_tab, const float* inv_tab,
-                         const GroupParams* prm, double* partials, int N, int K, int OUT, int nt,
-                         int no, int n_grid) {
+static void launch_tiles(bool pp, int tile_m, int64_t units, hipStream_t stream,
+                         const _Float16* X, const _Float16* W, const float* s_tab,
+                         const float* inv_tab, const GroupParams* prm, double* partials, int N,
+                         int K, int OUT, int nt, int no, int n_grid) {
   switch (tile_m) {
     case 512:
-      launch_split<512, 8, 256, 8, GS>(units, stream, X, W, s_tab, inv_tab, prm, partials, N, K,
-                                       OUT, nt, no, n_grid);
+      launch_split<512, 8, 256, 8, GS>(pp, units, stream, X, W, s_tab, inv_tab, prm, partials, N,
+                                       K, OUT, nt, no, n_grid);
       break;
     case 256:
-      launch_split<256, 8, 128, 4, GS>(units, stream, X, W, s_tab, inv_tab, prm, partials, N, K,
-                                       OUT, nt, no, n_grid);
+      launch_split<256, 8, 128, 4, GS>(pp, units, stream, X, W, s_tab, inv_tab, prm, partials, N,
+                                       K, OUT, nt, no, n_grid);
       break;
     default:
-      launch_one<128, 4, GS>((unsigned)units, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials,
-                             N, K, OUT, nt, no, n_grid);
+      launch_one<128, 4, GS>(pp, (unsigned)units, 0, 1, stream, X, W, s_tab, inv_tab, prm,
+                             partials, N, K, OUT, nt, no, n_grid);
       break;
   }
 }
@@ -428,15 +784,17 @@ void launch_grid(int tile_m, int group, const void* X, const void* W, const floa
   const int64_t units = (nt * no + 7) / 8 * 8 * n_grid;
   const _Float16* Xh = (const _Float16*)X;
   const _Float16* Wh = (const _Float16*)W;
+  const uintptr_t ds = (uintptr_t)inv_tab - (uintptr_t)s_tab;
+  const bool pp = (uintptr_t)inv_tab > (uintptr_t)s_tab && ds < ((uintptr_t)1 << 31);
   if (group == 32)
-    launch_tiles<1>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
-                    (int)OUT, (int)nt, (int)no, n_grid);
+    launch_tiles<1>(pp, tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
+                    (int)K, (int)OUT, (int)nt, (int)no, n_grid);
   else if (group == 64)
-    launch_tiles<2>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
-                    (int)OUT, (int)nt, (int)no, n_grid);
+    launch_tiles<2>(pp, tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
+                    (int)K, (int)OUT, (int)nt, (int)no, n_grid);
   else
-    launch_tiles<4>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
-                    (int)OUT, (int)nt, (int)no, n_grid);
+    launch_tiles<4>(pp, tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
+                    (int)K, (int)OUT, (int)nt, (int)no, n_grid);
 }
 
 }  // namespace awq
