@@ -559,7 +559,11 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   // fragments, then refills its activation buffer with chunk r/2 + 1; its
   // weight load for chunk (r+5)/2; for r % 4 == 1 its group's data for column
   // group (r+3)/4.
+  // The multiplying wavefront runs at raised priority, so that on its SIMD
+  // the other wavefront's VALU work fills the gaps between MFMAs rather than
+  // delaying them.
   auto multiply = [&](const half8 (&av)[MBW], int r, int s) {
+    __builtin_amdgcn_s_setprio(1);
     if (s == 0) read_a(a1, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfma_rows(av, 0, MBW / 2);
@@ -572,6 +576,8 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
     if ((r & 3) == 1) dma_g((r + 3) / 4);
     __builtin_amdgcn_sched_barrier(0);
     mfma_rows(av, MBW / 2, MBW);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
   // preparation of step r: this wavefront's part of dW(r+1) into `nxt`, the B
   // fragments of step r (dW(r) in `cur`) and for s == 0 its A fragments
