@@ -198,11 +198,13 @@ def test_search_edge_shapes(awq, n, k, o, n_grid):
     check_best(int(host(res.best_idx)[0]), ref.losses)
 
 
-@pytest.mark.parametrize("n,k,o", [(700, 256, 2048), (300, 256, 2048)])
+@pytest.mark.parametrize("n,k,o", [(700, 256, 2048), (300, 256, 2048), (700, 256, 2000),
+                                   (1000, 384, 1970)])
 def test_search_split_last_round(awq, n, k, o):
     """Shapes whose work units fill the chip 2.5 times: the last half round runs
-    as half-height tiles, and the second half of the ragged last token tile is
-    empty."""
+    as half-height tiles, with ragged token tiles (the second half of the last
+    one can be empty) and ragged last output tiles (2000 = 15 x 128 + 80,
+    1970 = 15 x 128 + 50)."""
     _say(f"search split last round {n}x{k}->{o}")
     _, X, W = synth.make_custom(n, k, o, seed=n + o)
     Xd, Wd, sal, res = run_layer(awq, X, W)
