@@ -8,7 +8,10 @@ prepare, fused grid kernel, select) and packing at the chosen alpha
 before timing starts.  The line printed on stdout:
 
   value        search flops of the step (20 grid points x 2 N in out, summed
-               over layers) / step time, TFLOP/s
+               over layers) / step time, TFLOP/s; the step time is the wall
+               clock of --steps steps run back to back (each search one call),
+               synchronized on both sides, after --warmup steps and an untimed
+               pass that records the per-stage events
   roofline     the dominant kernel (the fused grid kernel): algorithmic flops
                per search / the mean time of the search's grid launches, from
                HIP events recorded on the launch stream, against the fp16 dense
@@ -387,8 +390,10 @@ def copy_calibration(mib):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the shader clock rises over the first ~10 ms of sustained load: 20 warm-up
+    # steps of the default layer reach the steady state
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -491,6 +496,9 @@ def main():
     names = ("stats", "prepare", "grid", "select", "pack")
 
     def step(events=None):
+        """One pass of the hot path over every layer: saliency, search, pack.  With
+        events, the search runs stage by stage with an event between stages (the
+        per-stage breakdown); without, as one call, the way a caller runs it."""
         for li, L in enumerate(layers):
             ev = events[li] if events is not None else None
 
@@ -500,7 +508,9 @@ def main():
             mark(0)
             awq.awq_act_stats(L["X"], out=L["sal"], workspace=L["sws"])
             mark(1)
-            for j, stg in enumerate((awq.STAGE_PREPARE, awq.STAGE_GRID, awq.STAGE_SELECT)):
+            stages = ((awq.STAGE_PREPARE, awq.STAGE_GRID, awq.STAGE_SELECT) if ev is not None
+                      else (awq.STAGE_ALL,))
+            for j, stg in enumerate(stages):
                 awq.awq_search_layer(L["X"], L["W"], L["sal"], cfg, workspace=L["ws"],
                                      losses=L["losses"], best_idx=L["best"],
                                      s_best=L["s_best"], stages=stg)
@@ -511,13 +521,18 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # events on torch's current stream, which is the stream every call launches on
+    # per-stage breakdown (untimed pass): events on torch's current stream, which is
+    # the stream every call launches on; each event costs a few microseconds of queue
+    # time, so the headline below is timed on a separate pass without them
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in layers]
            for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(args.steps):
         step(evs[s])
+    torch.cuda.synchronize()
+    # the timed region: exactly args.steps steps, synchronized on both sides
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
