@@ -149,8 +149,9 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
 #pragma unroll
     for (int r = 0; r < RW; ++r) orow[r] = min(ob + r * waves, OUT - 1);  // past the end: repeat
     // the pass's codes, steps and zeros are all requested before any is used
+    // (a slice's step and zero share one register)
     uint4 cw[RW][SL];
-    _Float16 sb[RW][SL], zb[RW][SL];
+    half2v sz[RW][SL];
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
       if (64 * i >= ns) break;  // wavefront-uniform
@@ -158,8 +159,8 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         cw[r][i] = qw[(size_t)orow[r] * ns + c];
-        sb[r][i] = step16[(size_t)orow[r] * ng + (c >> 2)];
-        zb[r][i] = zero16[(size_t)orow[r] * ng + (c >> 2)];
+        sz[r][i].x = step16[(size_t)orow[r] * ng + (c >> 2)];
+        sz[r][i].y = zero16[(size_t)orow[r] * ng + (c >> 2)];
       }
     }
     float y[RW][MT];
@@ -182,8 +183,8 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
         }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-          const float st = (float)sb[r][i];
-          const float zr = (float)zb[r][i];
+          const float st = (float)sz[r][i].x;
+          const float zr = (float)sz[r][i].y;
           const uint32_t w[4] = {cw[r][i].x, cw[r][i].y, cw[r][i].z, cw[r][i].w};
           float d[MT];
 #pragma unroll
@@ -242,13 +243,41 @@ static void launch_gemv(const _Float16* X, int M, int K, int OUT, const uint4* q
                      M, K, OUT, qw, st, zr, Y);
 }
 
+// SL = 16-byte code loads per lane per row, the smallest of 2, 3, 4, 6, 8 that
+// covers the row (K <= 64 * SL * 32); RW rows per wavefront and pass, enough
+// for two blocks per compute unit to hold every row in one pass (at most 4).
+template <int MT, int SL>
+static void launch_gemv_rw(const _Float16* X, int M, int K, int OUT, const uint4* qw,
+                           const _Float16* st, const _Float16* zr, float* Y, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    cus = 256;
+  const int waves = 2 * cus * (kGemvThreads / 64);
+  const int rw = (OUT + waves - 1) / waves;
+  if (rw <= 1)
+    launch_gemv<MT, SL, 1>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else if (rw <= 2 || SL > 4)
+    launch_gemv<MT, SL, 2>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else
+    launch_gemv<MT, SL, 4>(X, M, K, OUT, qw, st, zr, Y, stream);
+}
+
 template <int MT>
 static void launch_gemv_k(const _Float16* X, int M, int K, int OUT, const uint4* qw,
                           const _Float16* st, const _Float16* zr, float* Y, hipStream_t stream) {
-  if (K <= 64 * 4 * 32)
-    launch_gemv<MT, 4, 4>(X, M, K, OUT, qw, st, zr, Y, stream);
+  const int sl = (K / 32 + 63) / 64;
+  if (sl <= 2)
+    launch_gemv_rw<MT, 2>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else if (sl <= 3)
+    launch_gemv_rw<MT, 3>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else if (sl <= 4)
+    launch_gemv_rw<MT, 4>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else if (sl <= 6)
+    launch_gemv_rw<MT, 6>(X, M, K, OUT, qw, st, zr, Y, stream);
   else
-    launch_gemv<MT, 8, 2>(X, M, K, OUT, qw, st, zr, Y, stream);
+    launch_gemv_rw<MT, 8>(X, M, K, OUT, qw, st, zr, Y, stream);
 }
 
 hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const int32_t* qweight,
