@@ -199,12 +199,12 @@ def test_search_edge_shapes(awq, n, k, o, n_grid):
 
 
 @pytest.mark.parametrize("n,k,o", [(700, 256, 2048), (300, 256, 2048), (700, 256, 2000),
-                                   (1000, 384, 1970)])
+                                   (700, 1024, 2048), (1000, 384, 1970)])
 def test_search_split_last_round(awq, n, k, o):
     """Shapes whose work units fill the chip 2.5 times: the last half round runs
     as half-height tiles, with ragged token tiles (the second half of the last
-    one can be empty) and ragged last output tiles (2000 = 15 x 128 + 80,
-    1970 = 15 x 128 + 50)."""
+    one can be empty), ragged last output tiles (2000 = 15 x 128 + 80,
+    1970 = 15 x 128 + 50) and one to eight column groups."""
     _say(f"search split last round {n}x{k}->{o}")
     _, X, W = synth.make_custom(n, k, o, seed=n + o)
     Xd, Wd, sal, res = run_layer(awq, X, W)
@@ -214,6 +214,26 @@ def test_search_split_last_round(awq, n, k, o):
     _say(f"  max rel loss diff {rel.max():.3e}")
     assert np.all(rel <= LOSS_RTOL)
     check_best(int(host(res.best_idx)[0]), ref.losses)
+
+
+def test_search_grid_stage_repeated(awq):
+    """The grid and select stages run again on the same workspace, with no new
+    preparation, give bitwise the same losses (and the oracle's): the stages keep
+    no state between launches beyond the prepared tables, and the partial sums
+    of a search (including its split last round) add in a fixed order."""
+    n, k, o = 700, 1024, 2048
+    _say(f"search grid stage repeated {n}x{k}->{o}")
+    _, X, W = synth.make_custom(n, k, o, seed=7)
+    Xd, Wd, sal, res = run_layer(awq, X, W)
+    assert res.plan.tile_tokens == 512
+    first = host(res.losses).copy()
+    ref = O.search_layer(X, W, host(sal))
+    assert np.all(np.abs(first - ref.losses) <= LOSS_RTOL * ref.losses)
+    for _ in range(3):
+        again = awq.awq_search_layer(Xd, Wd, sal, workspace=res.workspace,
+                                     stages=awq._lib.STAGE_GRID | awq._lib.STAGE_SELECT)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(again.losses).view(np.uint64), first.view(np.uint64))
 
 
 def test_search_degenerate_inputs(awq):
