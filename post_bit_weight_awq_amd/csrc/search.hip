@@ -115,15 +115,18 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     const float4 v = ((const float4*)(s_tab + (size_t)i * K + g * G))[c4];
     s_lds4[i * PG4 + (c4 / (PL / 4)) * CH4 + c4 % (PL / 4)] = v;
   }
+  // the lane's weights, widened to fp32 once (exact) for the whole grid loop
   const uint4* wp = (const uint4*)(W + (size_t)o * K + k0);
-  uint32_t w[PL / 2];
+  float wf[PL];
 #pragma unroll
   for (int v = 0; v < PL / 8; ++v) {
     const uint4 t = wp[v];
-    w[4 * v] = t.x;
-    w[4 * v + 1] = t.y;
-    w[4 * v + 2] = t.z;
-    w[4 * v + 3] = t.w;
+    const uint32_t u[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wf[8 * v + 2 * e] = f16_lo(u[e]);
+      wf[8 * v + 2 * e + 1] = f16_hi(u[e]);
+    }
   }
   const float half = 0.5f * (qmax + 1.0f);  // 2^(b-1)
   __syncthreads();
@@ -134,24 +137,23 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     for (int j = 0; j < 4; ++j) {
       const int i = min(i0 + j, n_grid - 1);
       const float4* sp = s_lds4 + i * PG4 + l4 * CH4;
+      // ws = fp32(w * s): the product of the exact fp32 widening, rounded once.
+      // The compiler knows products are canonical, so fminf / fmaxf chains
+      // become v_min3 / v_max3 with no canonicalizing instructions.
       float mn, mx;
 #pragma unroll
       for (int v = 0; v < PL / 4; ++v) {
         const float4 sv = sp[v];
-        const float a = mul_f16_f32<false>(w[2 * v], sv.x, nz);
-        const float b = mul_f16_f32<true>(w[2 * v], sv.y, nz);
-        const float c = mul_f16_f32<false>(w[2 * v + 1], sv.z, nz);
-        const float d = mul_f16_f32<true>(w[2 * v + 1], sv.w, nz);
+        const float a = wf[4 * v] * sv.x;
+        const float b = wf[4 * v + 1] * sv.y;
+        const float c = wf[4 * v + 2] * sv.z;
+        const float d = wf[4 * v + 3] * sv.w;
         if (v == 0) {
-          mn = min3f(a, b, c);
-          mx = max3f(a, b, c);
-          mn = min3f(mn, d, d);
-          mx = max3f(mx, d, d);
+          mn = fminf(fminf(a, b), fminf(c, d));
+          mx = fmaxf(fmaxf(a, b), fmaxf(c, d));
         } else {
-          mn = min3f(mn, a, b);
-          mx = max3f(mx, a, b);
-          mn = min3f(mn, c, d);
-          mx = max3f(mx, c, d);
+          mn = fminf(fminf(mn, a), fminf(b, fminf(c, d)));
+          mx = fmaxf(fmaxf(mx, a), fmaxf(b, fmaxf(c, d)));
         }
       }
       mnv[j] = mn;

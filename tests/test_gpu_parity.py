@@ -163,6 +163,39 @@ def test_search_matches_oracle(awq, name, kw):
     assert np.array_equal(st.view(np.uint16), pref.step16.view(np.uint16))
 
 
+@pytest.mark.parametrize("n,k,o", [(64, 1024, 300), (16, 384, 77)])
+def test_group_params_bit_exact(awq, n, k, o):
+    """The per-group quantizer parameters the preparation stage leaves in the
+    workspace (binary32 step, 1/step, -zero, 15 - zero for every grid point,
+    column group and output row) equal the oracle's quantizer applied to
+    fp32(W diag(s_i)), bit for bit.  Offsets: the workspace holds the partial
+    sums, the scale table, the reciprocal table and the parameters, in that
+    order, each region starting on a 256-byte boundary."""
+    _say(f"group params {n}x{k}->{o}")
+    _, X, W = synth.make_custom(n, k, o, seed=n + k)
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    res = awq.awq_search_layer(Xd, Wd, sal, stages=awq._lib.STAGE_PREPARE)
+    torch.cuda.synchronize()
+    n_grid, ng = 20, k // 128
+    a256 = lambda v: (v + 255) // 256 * 256
+    off_inv = a256(res.plan.scales_offset + 4 * n_grid * k)
+    off_prm = a256(off_inv + 4 * n_grid * k)
+    prm = host(res.workspace[off_prm:off_prm + 16 * n_grid * ng * o].view(torch.float32))
+    prm = prm.reshape(n_grid, ng, o, 4)
+    s_tab, _ = O.scale_table(host(sal))
+    for i in range(n_grid):
+        gq = O.quantize(O.scaled_weights(W, s_tab[i]))
+        step = gq.step.T  # [ng, o]
+        zero = gq.zero.T
+        got = prm[i]
+        assert np.array_equal(got[..., 0].view(np.uint32), step.view(np.uint32)), i
+        inv = (np.float32(1) / step).astype(np.float32)
+        assert np.array_equal(got[..., 1].view(np.uint32), inv.view(np.uint32)), i
+        assert np.array_equal(got[..., 2], -zero), i
+        assert np.array_equal(got[..., 3], np.float32(15) - zero), i
+
+
 def test_search_is_deterministic(awq):
     _, X, W = synth.make_layer(3, n_tokens=256, out_features=512)
     Xd, Wd = dev(X), dev(W)
