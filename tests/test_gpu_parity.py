@@ -80,7 +80,7 @@ def test_stats_bitexact_configs(awq, cfg, layer):
     assert np.array_equal(sal.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("n,k", [(1, 8), (37, 520), (3, 4096), (1000, 136), (9000, 64)])
+@pytest.mark.parametrize("n,k", [(1, 8), (37, 520), (3, 4096), (1000, 136), (8192, 512), (9000, 64)])
 def test_stats_edge_shapes(awq, n, k):
     _say(f"stats edge {n}x{k}")
     rng = np.random.default_rng(n * 7 + k)
