@@ -148,21 +148,35 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
     int orow[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) orow[r] = min(ob + r * waves, OUT - 1);  // past the end: repeat
-    // the pass's codes, steps and zeros are all requested before any is used
-    // (a slice's step and zero share one register)
+    // The pass's steps and zeros, then its codes in the order the arithmetic
+    // takes them, are all requested before any is used.  Steps and zeros stay
+    // in registers of their own (each converted where it is used, so nothing
+    // waits for them early), and each slice's arithmetic waits only for its
+    // own codes: it starts while later codes still stream in.  Slices past the
+    // row's end re-read its last slice and count with step 0, so loads and
+    // arithmetic are straight-line code (branches here made the compiler wait
+    // for every load before the first product, or sink loads into them).
     uint4 cw[RW][SL];
-    half2v sz[RW][SL];
+    _Float16 stp[RW][SL], zrp[RW][SL];
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
-      if (64 * i >= ns) break;  // wavefront-uniform
       const int c = min(lane + 64 * i, ns - 1);
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
-        cw[r][i] = qw[(size_t)orow[r] * ns + c];
-        sz[r][i].x = step16[(size_t)orow[r] * ng + (c >> 2)];
-        sz[r][i].y = zero16[(size_t)orow[r] * ng + (c >> 2)];
+        stp[r][i] = step16[(size_t)orow[r] * ng + (c >> 2)];
+        zrp[r][i] = zero16[(size_t)orow[r] * ng + (c >> 2)];
       }
     }
+#pragma unroll
+    for (int i = 0; i < SL; ++i) {
+      const int c = min(lane + 64 * i, ns - 1);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        __builtin_amdgcn_sched_barrier(0);
+        cw[r][i] = qw[(size_t)orow[r] * ns + c];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float y[RW][MT];
 #pragma unroll
     for (int r = 0; r < RW; ++r)
@@ -170,21 +184,17 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
       for (int t = 0; t < MT; ++t) y[r][t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
-      const int c = lane + 64 * i;
-      if (64 * i >= ns) break;  // wavefront-uniform
-      if (c < ns) {
-        uint4 xv[MT][4];
+      // a slice past the row's end takes step 0: its finite contribution is +0
+      const bool live = lane + 64 * i < ns;
+      const int c = min(lane + 64 * i, ns - 1);
+      {
         float xs[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xv[t][j] = lds[t * n8 + 4 * c + j];
-          xs[t] = xsum[t * ns + c];
-        }
+        for (int t = 0; t < MT; ++t) xs[t] = xsum[t * ns + c];
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-          const float st = (float)sz[r][i].x;
-          const float zr = (float)sz[r][i].y;
+          const float st = live ? (float)stp[r][i] : 0.0f;
+          const float zr = (float)zrp[r][i];
           const uint32_t w[4] = {cw[r][i].x, cw[r][i].y, cw[r][i].z, cw[r][i].w};
           float d[MT];
 #pragma unroll
@@ -196,7 +206,8 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
             for (int h = 0; h < 4; ++h) p[h] = sub_f16x2(((w[j] >> (4 * h)) & 0x000F000Fu) | kBias, kBias);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-              const uint32_t xp[4] = {xv[t][j].x, xv[t][j].y, xv[t][j].z, xv[t][j].w};
+              const uint4 xq = lds[t * n8 + 4 * c + j];
+              const uint32_t xp[4] = {xq.x, xq.y, xq.z, xq.w};
 #pragma unroll
               for (int h = 0; h < 4; ++h)
                 d[t] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, p[h]),
