@@ -22,6 +22,10 @@
 //     products; the group adds step * (A - z S) to the output.  The zero
 //     point enters as one multiply per group, so it may be any stored fp16
 //     value.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "awq_device.h"
 #include "awq_internal.h"
 
@@ -238,39 +242,73 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
   }
 }
 
+// Blocks of k_w4a16_gemv<MT, SL, RW> resident per compute unit on the current
+// device, from the runtime's occupancy query (cached per device and kernel).
 template <int MT, int SL, int RW>
-static void launch_gemv(const _Float16* X, int M, int K, int OUT, const uint4* qw,
-                        const _Float16* st, const _Float16* zr, float* Y, hipStream_t stream) {
-  const size_t lds = (size_t)MT * (K / 8) * 16 + (size_t)MT * (K / 32) * 4;
+static int gemv_blocks_per_cu(int dev, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, size_t>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, lds);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_w4a16_gemv<MT, SL, RW>,
+                                                   kGemvThreads, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  cache[key] = per_cu;
+  return per_cu;
+}
+
+static int device_cus(int* dev_out) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1)
     cus = 256;
+  *dev_out = dev;
+  return cus;
+}
+
+static size_t gemv_lds(int MT, int K) { return (size_t)MT * (K / 8) * 16 + (size_t)MT * (K / 32) * 4; }
+
+// Rows the RW-row kernel covers in one round of resident blocks.
+template <int MT, int SL, int RW>
+static int64_t gemv_round_rows(int K) {
+  int dev = 0;
+  const int cus = device_cus(&dev);
+  return (int64_t)gemv_blocks_per_cu<MT, SL, RW>(dev, gemv_lds(MT, K)) * cus *
+         (kGemvThreads / 64) * RW;
+}
+
+template <int MT, int SL, int RW>
+static void launch_gemv(const _Float16* X, int M, int K, int OUT, const uint4* qw,
+                        const _Float16* st, const _Float16* zr, float* Y, hipStream_t stream) {
+  const size_t lds = gemv_lds(MT, K);
+  int dev = 0;
+  const int cus = device_cus(&dev);
   const int rows_per_block = RW * (kGemvThreads / 64);
   const int want = (OUT + rows_per_block - 1) / rows_per_block;
-  const int blocks = want < 2 * cus ? want : 2 * cus;
+  const int resident = gemv_blocks_per_cu<MT, SL, RW>(dev, lds) * cus;
+  const int blocks = want < resident ? want : resident;
   hipLaunchKernelGGL((k_w4a16_gemv<MT, SL, RW>), dim3(blocks), dim3(kGemvThreads), lds, stream, X,
                      M, K, OUT, qw, st, zr, Y);
 }
 
 // SL = 16-byte code loads per lane per row, the smallest of 2, 3, 4, 6, 8 that
-// covers the row (K <= 64 * SL * 32); RW rows per wavefront and pass, enough
-// for two blocks per compute unit to hold every row in one pass (at most 4).
+// covers the row (K <= 64 * SL * 32); RW rows per wavefront and pass, the
+// fewest (1, 2, 3 or 4; at most 3 for SL > 4, whose registers allow no more)
+// with which the resident blocks hold every row in one pass, else the most.
 template <int MT, int SL>
 static void launch_gemv_rw(const _Float16* X, int M, int K, int OUT, const uint4* qw,
                            const _Float16* st, const _Float16* zr, float* Y, hipStream_t stream) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    cus = 256;
-  const int waves = 2 * cus * (kGemvThreads / 64);
-  const int rw = (OUT + waves - 1) / waves;
-  if (rw <= 1)
+  if (OUT <= gemv_round_rows<MT, SL, 1>(K))
     launch_gemv<MT, SL, 1>(X, M, K, OUT, qw, st, zr, Y, stream);
-  else if (rw <= 2 || SL > 4)
+  else if (OUT <= gemv_round_rows<MT, SL, 2>(K))
     launch_gemv<MT, SL, 2>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else if (OUT <= gemv_round_rows<MT, SL, 3>(K) || SL > 4)
+    launch_gemv<MT, SL, 3>(X, M, K, OUT, qw, st, zr, Y, stream);
   else
     launch_gemv<MT, SL, 4>(X, M, K, OUT, qw, st, zr, Y, stream);
 }

@@ -349,8 +349,11 @@ def _w4a16_check(awq, x, qw, st, zr):
     return y, want
 
 
+# (1, 12416, 4100): 388 slices per row, so the eighth load per lane lies past
+# the row and the seventh covers 4 lanes; 4100 rows take three rows per
+# wavefront and pass with the last pass ragged
 W4_CASES = [(1, 4096, 4096), (3, 384, 17), (16, 128, 16), (17, 256, 33), (40, 5120, 300),
-            (1, 13824, 64), (2, 128, 1)]
+            (1, 13824, 64), (1, 12416, 4100), (2, 128, 1)]
 
 
 @pytest.mark.parametrize("m,k,o", W4_CASES)
