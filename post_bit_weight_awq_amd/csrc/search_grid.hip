@@ -13,10 +13,10 @@
 // of dW has relative size <= 2^-11 and zero mean; it changes a loss by a
 // second-order amount (measured ~1e-6 relative).
 //
-// Two kernels share this file.  k_grid_pp (after k_grid) runs groups of 128
-// columns on the 512- and 256-token tiles; k_grid runs groups of 32 and 64
-// columns and the 128-token tile.  The notes below describe k_grid; those of
-// k_grid_pp stand above it.
+// Two kernels share this file.  k_grid_pp (after k_grid) runs the 512- and
+// 256-token tiles, for groups of 32, 64 and 128 columns; k_grid runs the
+// 128-token tile.  The notes below describe k_grid; those of k_grid_pp stand
+// above it.
 //
 // Layout (BM tokens x BN outputs per block, NW wavefronts, K steps of 32):
 //   * NW wavefronts stacked along tokens (8 for the 512- and 256-token tiles,
@@ -385,7 +385,7 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
 // before every LDS read; at the end of each multiply phase a wavefront waits
 // for all of its loads except that phase's own.  Nothing else in the loop
 // uses the vector memory counter, which keeps those counts exact.
-template <int BM, int BN>
+template <int BM, int BN, int GS>
 __global__ void __launch_bounds__(512, 1)
 k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
           const float* __restrict__ s_tab, const float* __restrict__ inv_tab,
@@ -394,7 +394,11 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   constexpr int NW = 8;
   constexpr int KC = 32;            // k per MFMA step
   constexpr int KCH = 64;           // k per load chunk
-  constexpr int GC = 128;           // columns per quantization group
+  constexpr int GC = 32 * GS;       // columns per quantization group (GS K steps)
+  // group-data slots: a group's data is loaded in the multiply phase of step
+  // GS*g - 3 (the latest from which it lands before dW(GS*g) is produced);
+  // groups of 32 need four slots for the group it replaces to be finished
+  constexpr int NGS = GS == 1 ? 4 : 2;
   constexpr int WMT = BM / NW;      // tokens per wavefront
   constexpr int MBW = WMT / 16;
   constexpr int NBW = BN / 16;
@@ -405,8 +409,8 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   __shared__ __attribute__((aligned(16))) _Float16 wq1[BN * LDW];
   __shared__ __attribute__((aligned(16))) _Float16 abuf[NW][WMT * KCH];  // per wavefront
   __shared__ __attribute__((aligned(16))) _Float16 wraw[3][BN * KCH];    // ring of chunks
-  __shared__ __attribute__((aligned(16))) float4 gprm[2][2][64];         // [slot][group][row]
-  __shared__ __attribute__((aligned(16))) float gscl[2][2][2 * GC];      // [slot][group] s | 1/s
+  __shared__ __attribute__((aligned(16))) float4 gprm[NGS][2][64];       // [slot][group][row]
+  __shared__ __attribute__((aligned(16))) float gscl[NGS][2][256];       // [slot][group] s | 1/s
   __shared__ double red[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -459,8 +463,11 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   const GroupParams* pgp = prm + (size_t)ai * ngroups * OUT;
   const uint32_t pgo = 16u * (uint32_t)min(o0 + 64 * grp + lane, OUT - 1);
   const float* pgs = s_tab + (size_t)ai * K;
-  const uint32_t pso = 16 * (lane & 31) +
-                       (lane < 32 ? 0u : (uint32_t)((const char*)inv_tab - (const char*)s_tab));
+  // lanes 0 .. GC/4-1 the group's scales, the next GC/4 lanes its reciprocals
+  // (further lanes repeat them: a load fills 64 x 16 bytes of LDS)
+  const int sl4 = lane % (GC / 2);
+  const uint32_t pso = 16 * (sl4 % (GC / 4)) +
+                       (sl4 < GC / 4 ? 0u : (uint32_t)((const char*)inv_tab - (const char*)s_tab));
 
   floatx4 acc[MBW][NBW];
 #pragma unroll
@@ -489,10 +496,14 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   auto dma_g = [&](int g) {
     const int src = min(g, ngroups - 1);
     if (pc == 0)
-      dma(pgp + (size_t)src * OUT, pgo, &gprm[g & 1][grp][0]);
+      dma(pgp + (size_t)src * OUT, pgo, &gprm[g % NGS][grp][0]);
     else if (pc == 1)
-      dma(pgs + src * GC, pso, &gscl[g & 1][grp][0]);
+      dma(pgs + src * GC, pso, &gscl[g % NGS][grp][0]);
   };
+  // whether step r's multiply phase loads group data, and how many loads the
+  // wavefront issues in that phase (its wait at the phase end keeps them)
+  auto g_phase = [&](int r) { return (r + 3) % GS == 0; };
+  const bool gw = pc < 2;
   // this wavefront's part of dW(step): piece pc of row prow.  Split in two so
   // that its LDS reads can be issued before other reads and its arithmetic
   // run while those land.
@@ -502,7 +513,7 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   };
   auto produce_in = [&](int step) {
     PIn p;
-    const int gs = (step >> 2) & 1, c = 8 * (step & 3) + 2 * pc;  // scale index / 4
+    const int gs = (step / GS) % NGS, c = 8 * (step % GS) + 2 * pc;  // scale index / 4
     const float4* sc = (const float4*)&gscl[gs][grp][0];
     p.s0 = sc[c];
     p.s1 = sc[c + 1];
@@ -590,10 +601,11 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
       }
       __builtin_amdgcn_sched_barrier(0);
       dma_w((r + 5) >> 1, (r + 1) & 1);
+      if (g_phase(r)) dma_g((r + 3) / GS);
     } else {
       if (s == 0) dma_a(r / 2 + 1);
       dma_w((r + 5) >> 1, (r + 1) & 1);
-      if ((r & 3) == 1) dma_g((r + 3) / 4);
+      if (g_phase(r)) dma_g((r + 3) / GS);
       __builtin_amdgcn_sched_barrier(0);
       mfma_rows(av, MBW / 2, MBW);
     }
@@ -629,18 +641,28 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
     store_piece(o, nxt);
   };
   // after a multiply phase: all loads but that phase's own (for s == 0 the
-  // activation chunk and a weight load, else a weight load and possibly the
-  // group data) have landed
+  // activation chunk and a weight load, else a weight load; possibly the group
+  // data) have landed.  For groups of 128 the group-data phases keep one load
+  // (the group data then waits for nothing, the weight load with it); for
+  // smaller groups, whose phases load group data far more often, the count is
+  // exact.
   auto end_phase = [&](int wait_keep) {
     __builtin_amdgcn_sched_barrier(0);
     if (wait_keep == 1) __builtin_amdgcn_s_waitcnt(0x0f71);
+    if (wait_keep == 2) __builtin_amdgcn_s_waitcnt(0x0f72);
     if (wait_keep == 1 + ALD) __builtin_amdgcn_s_waitcnt(0x0f70 | (1 + ALD));
+    if (wait_keep == 2 + ALD) __builtin_amdgcn_s_waitcnt(0x0f70 | (2 + ALD));
     __syncthreads();
   };
+  auto keep = [&](int r, int s) {
+    const int own = s == 0 ? 1 + ALD : 1;
+    return own + (GS < 4 && gw && g_phase(r) ? 1 : 0);
+  };
 
-  // prologue: group data 0, activation chunk 0, weight chunks 0..2 of the
-  // group's rows; all of dW(0)
-  dma_g(0);
+  // prologue: the group data the loop does not load (groups 0 .. ceil(3/GS)-1),
+  // activation chunk 0, weight chunks 0..2 of the group's rows; all of dW(0)
+#pragma unroll
+  for (int g = 0; g < (3 + GS - 1) / GS; ++g) dma_g(g);
   dma_a(0);
 #pragma unroll
   for (int c = 0; c < 3; ++c) {
@@ -659,11 +681,11 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
     end_phase(0);
     for (int k = 0; k < nk; k += 2) {
       multiply(a0, k, 0);           // phase 2k: step k
-      end_phase(1 + ALD);
+      end_phase(keep(k, 0));
       prepare(k + 1, 1, wq1, wq0);  // phase 2k+1
       end_phase(0);
       multiply(a1, k + 1, 1);       // phase 2k+2: step k+1
-      end_phase(1);
+      end_phase(keep(k + 1, 1));
       prepare(k + 2, 0, wq0, wq1);  // phase 2k+3
       end_phase(0);
     }
@@ -673,11 +695,11 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
       prepare(k, 0, wq0, wq1);      // phase 2k
       end_phase(0);
       multiply(a0, k, 0);           // phase 2k+1: step k
-      end_phase(1 + ALD);
+      end_phase(keep(k, 0));
       prepare(k + 1, 1, wq1, wq0);  // phase 2k+2
       end_phase(0);
       multiply(a1, k + 1, 1);       // phase 2k+3: step k+1
-      end_phase(1);
+      end_phase(keep(k + 1, 1));
     }
   }
   // the last loads (re-reads, never used) land before the block ends
@@ -737,7 +759,7 @@ int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
 // table (it reaches both through one base address); otherwise k_grid runs.
 template <int NW, int GS>
 static constexpr bool pp_shape() {
-  return GS == 4 && NW == 8;
+  return NW == 8;
 }
 
 template <int BM, int NW, int GS>
@@ -747,7 +769,7 @@ static void launch_one(bool pp, unsigned blocks, int unit_base, int split, hipSt
                        int K, int OUT, int nt, int no, int n_grid) {
   if constexpr (pp_shape<NW, GS>()) {
     if (pp) {
-      hipLaunchKernelGGL((k_grid_pp<BM, kGridBN>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
+      hipLaunchKernelGGL((k_grid_pp<BM, kGridBN, GS>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
                          s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base,
                          split);
       return;
@@ -774,7 +796,7 @@ static int64_t resident_blocks(bool pp) {
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) {
     if (pp)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid_pp<BM, kGridBN>, NW * 64,
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid_pp<BM, kGridBN, GS>, NW * 64,
                                                        0);
     else
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid<BM, kGridBN, NW, GS>,

@@ -473,6 +473,29 @@ def test_variant_search_and_pack_match_oracle(awq, group, w_bit, zp):
     assert np.array_equal(zr.view(np.uint16), pref.zero16.view(np.uint16))
 
 
+@pytest.mark.parametrize("n,k,o,group,w_bit,zp", [(700, 1024, 2048, 64, 4, True),
+                                                  (700, 1024, 2000, 32, 4, True),
+                                                  (1000, 640, 1970, 32, 3, False)])
+def test_variant_split_last_round(awq, n, k, o, group, w_bit, zp):
+    """Groups of 64 and 32 columns on the 512-token tile with the partial last
+    round on the 256-token tile (ragged token tiles and last output tiles): all
+    losses against the oracle."""
+    _say(f"variant split last round {n}x{k}->{o} group {group} w_bit {w_bit} zp {zp}")
+    _, X, W = synth.make_custom(n, k, o, seed=n + o + group)
+    cfg = awq.default_config(group_size=group, w_bit=w_bit, zero_point=zp)
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    res = awq.awq_search_layer(Xd, Wd, sal, cfg)
+    torch.cuda.synchronize()
+    assert res.plan.tile_tokens == 512
+    ref = O.search_layer(X, W, host(sal), group=group, w_bit=w_bit, zero_point=zp)
+    losses = host(res.losses)
+    rel = np.abs(losses - ref.losses) / ref.losses
+    _say(f"  max rel loss diff {rel.max():.3e}")
+    assert np.all(rel <= LOSS_RTOL)
+    check_best(int(host(res.best_idx)[0]), ref.losses)
+
+
 @pytest.mark.parametrize("group,w_bit,zp", [(64, 3, True), (32, 4, False)])
 def test_variant_full_size_sampled_tiles(awq, group, w_bit, zp):
     spec, X, W = synth.make_layer(2, 0)
