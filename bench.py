@@ -77,7 +77,7 @@ def grid_kernel_names(layers, cfg):
     for L in layers:
         sp = L["spec"]
         plan = P.awq_search_plan(sp.n_tokens, sp.in_features, sp.out_features, cfg)
-        nm = "k_grid_pp" if cfg.group_size == 128 and plan.tile_tokens in (512, 256) else "k_grid"
+        nm = "k_grid_pp" if plan.tile_tokens in (512, 256) else "k_grid"
         if nm not in names:
             names.append(nm)
     return " + ".join(names)
