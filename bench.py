@@ -71,7 +71,7 @@ def source_digest():
 
 def grid_kernel_names(layers, cfg):
     """Names of the grid-stage kernels the searches launch: the ping-pong
-    kernel for groups of 128 columns on 512- and 256-token tiles, else k_grid."""
+    kernel on 512- and 256-token tiles, else k_grid."""
     import post_bit_weight_awq_amd as P
     names = []
     for L in layers:
