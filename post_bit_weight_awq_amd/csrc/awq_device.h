@@ -18,18 +18,24 @@ constexpr int kGroup = 128;
 // included), so those FMAs are exact products with a single rounding.
 __device__ __forceinline__ float neg_zero() { return __uint_as_float(0x80000000u); }
 
+// -0.0f in a register whose value the compiler cannot see.  Passed as the
+// addend of mul_f16_f32, it keeps that function one mixed-precision FMA
+// (v_fma_mix_f32): with a known -0 the compiler would fold the FMA into a
+// conversion and a multiply.  Take it once per kernel.
+__device__ __forceinline__ float opaque_neg_zero() {
+  float r;
+  asm volatile("v_mov_b32 %0, 0x80000000" : "=v"(r));
+  return r;
+}
+
 // fp32(h * s) where h is the low (HI=false) or high (HI=true) fp16 half of `w2`.
-// The fp16 operand is widened exactly, so this equals fp32(fp32(h) * s).
+// The fp16 operand is widened exactly and nz is -0, so this equals
+// fp32(fp32(h) * s) with a single rounding; written in C so the compiler
+// knows the instruction it selects (no padding for an unknown inline asm).
 template <bool HI>
 __device__ __forceinline__ float mul_f16_f32(uint32_t w2, float s, float nz) {
-  float r;
-  if (HI)
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=v"(r) : "v"(w2), "v"(s), "v"(nz));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
-        : "=v"(r) : "v"(w2), "v"(s), "v"(nz));
-  return r;
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(HI ? (w2 >> 16) : (w2 & 0xffffu)));
+  return __builtin_fmaf((float)h, s, nz);
 }
 
 // The same with a wavefront-uniform scale held in a scalar register (saves the

@@ -48,7 +48,7 @@ k_pack(const uint4* __restrict__ W, const float* __restrict__ s, int64_t OUT, in
     widx[u] = (o * K + k0[u]) / 8;
     w[u] = W[widx[u]];
   }
-  const float nz = neg_zero();
+  const float nz = opaque_neg_zero();
 #pragma unroll
   for (int u = 0; u < kPackPerTeam; ++u) {
     const float4 sa = *(const float4*)(s + k0[u]), sb = *(const float4*)(s + k0[u] + 4);

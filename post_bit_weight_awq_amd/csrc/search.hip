@@ -130,7 +130,6 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
   }
   const float half = 0.5f * (qmax + 1.0f);  // 2^(b-1)
   __syncthreads();
-  const float nz = neg_zero();
   for (int i0 = 0; i0 < n_grid; i0 += 4) {
     float mnv[4], mxv[4];
 #pragma unroll

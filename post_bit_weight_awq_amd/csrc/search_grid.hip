@@ -107,7 +107,7 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   }
   const int ngroups = K / (KC * GS);  // quantization groups of 32 * GS columns
   const int nk = K / KC;               // a multiple of 4
-  const float nz = neg_zero();
+  const float nz = opaque_neg_zero();
 
   // activation rows of this lane, as 32-bit offsets from the tile's first row
   // (rows past the end re-read the last row; their outputs are masked in the
@@ -431,7 +431,7 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   const int ngroups = K / GC;
   const int nk = K / KC;     // a multiple of 4
   const int nch = K / KCH;   // chunks
-  const float nz = neg_zero();
+  const float nz = opaque_neg_zero();
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int grp = wv >> 2;   // 0: multiplies first; 1: prepares first
   const int pc = wv & 3;     // the wavefront's 8-column piece of a step in production
