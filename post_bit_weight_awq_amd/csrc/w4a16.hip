@@ -7,13 +7,17 @@
 // "AWQ > Salient Weight Preservation", step-size equation).
 //
 // HBM-bound at decode sizes: 0.5 byte of codes + 4/128 byte of step and zero
-// per weight, read once.  A block owns 16 output rows and 16 token rows; its
-// 16 wavefronts split the groups of 128 columns evenly and their partial
-// outputs are added in LDS at the end (fixed order, no atomics).
-//   * Lane l holds output row o0 + l % 16 and the 32-column slice l / 16 of the
-//     current group: one 16-byte load of 32 codes.  Each of its four words
-//     feeds one v_mfma_f32_16x16x32_f16 as the B operand; lane l's A operand is
-//     the matching 8 activations of token t0 + l % 16.
+// per weight, read once.  A block (the MFMA kernel, k_w4a16, for more than 4
+// tokens) owns 32 output rows, as two 16-row tiles, and 16 token rows; its 4
+// wavefronts split the groups of 128 columns evenly and their partial outputs
+// are added in LDS at the end (fixed order, no atomics).  The two row tiles
+// share each group's activation fragments (the activations are re-read per
+// block, so the tiles halve that traffic), and a wavefront requests the next
+// group's codes, activations, steps and zeros before this group's arithmetic.
+//   * Lane l holds output row o0 + 16 u + l % 16 of tile u and the 32-column
+//     slice l / 16 of the current group: one 16-byte load of 32 codes.  Each of
+//     its four words feeds one v_mfma_f32_16x16x32_f16 as the B operand; lane
+//     l's A operand is the matching 8 activations of token t0 + l % 16.
 //   * Codes become exact fp16 integers by bit placement: (nibble | 0x6400)
 //     is the fp16 value 1024 + nibble, and one packed fp16 subtraction of 1024
 //     leaves the code itself.  Two bit-select steps put them in column order.
@@ -31,7 +35,9 @@
 
 namespace awq {
 
-constexpr int kW4Slices = 16;  // wavefronts per block, each a share of the groups
+constexpr int kW4Slices = 4;   // wavefronts per block, each a share of the groups
+constexpr int kW4Tiles = 2;    // 16-row output tiles per wavefront (sharing the activations)
+constexpr int kW4Rows = 16 * kW4Tiles;  // output rows per block
 
 __device__ __forceinline__ uint32_t lo_lo(uint32_t a, uint32_t b) {
   return (a & 0xffffu) | (b << 16);
@@ -44,62 +50,103 @@ __global__ void __launch_bounds__(kW4Slices * 64)
 k_w4a16(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __restrict__ qw,
         const _Float16* __restrict__ step16, const _Float16* __restrict__ zero16,
         float* __restrict__ Y) {
-  __shared__ float red[kW4Slices][256];
+  __shared__ float red[kW4Slices][kW4Rows * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int o0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int o0 = blockIdx.x * kW4Rows, t0 = blockIdx.y * 16;
   const int r16 = lane & 15, j4 = lane >> 4;
-  const int orow = min(o0 + r16, OUT - 1);  // rows past the end re-read the last row
   const int tok = t0 + r16;
   const bool tok_ok = tok < M;
   const int ng = K >> 7;
   const int g0 = (int)((int64_t)wave * ng / kW4Slices);
   const int g1 = (int)((int64_t)(wave + 1) * ng / kW4Slices);
-  const uint4* qrow = qw + (size_t)orow * (K >> 5) + j4;  // group g at qrow[4 g]
   const _Float16* xrow = X + (size_t)(tok_ok ? tok : 0) * K + 32 * j4;
-  const _Float16* srow = step16 + (size_t)orow * ng;
-  const _Float16* zrow = zero16 + (size_t)orow * ng;
+  const uint4* qrow[kW4Tiles];
+  const _Float16* srow[kW4Tiles];
+  const _Float16* zrow[kW4Tiles];
+#pragma unroll
+  for (int u = 0; u < kW4Tiles; ++u) {
+    const int orow = min(o0 + 16 * u + r16, OUT - 1);  // rows past the end re-read the last row
+    qrow[u] = qw + (size_t)orow * (K >> 5) + j4;  // group g at qrow[u][4 g]
+    srow[u] = step16 + (size_t)orow * ng;
+    zrow[u] = zero16 + (size_t)orow * ng;
+  }
   constexpr uint32_t kBias = 0x64006400u;  // fp16 1024 in both halves
   half8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.0f;
-  floatx4 y = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int g = g0; g < g1; ++g) {
-    const uint4 q = qrow[4 * g];
+  floatx4 y[kW4Tiles];
+#pragma unroll
+  for (int u = 0; u < kW4Tiles; ++u) y[u] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  floatx4 sum_x = {0.0f, 0.0f, 0.0f, 0.0f};
+  // one group's operands; the next group's are requested before this group's
+  // arithmetic (groups past the wavefront's range re-read its last group)
+  struct Ops {
+    uint4 q[kW4Tiles];
     uint4 xv[4];
+    _Float16 st[kW4Tiles], zr[kW4Tiles];
+  };
+  auto load = [&](Ops& o, int g) {
+    g = min(g, g1 - 1);
+#pragma unroll
+    for (int u = 0; u < kW4Tiles; ++u) {
+      o.st[u] = srow[u][g];
+      o.zr[u] = zrow[u][g];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      xv[j] = tok_ok ? *(const uint4*)(xrow + 128 * g + 8 * j) : make_uint4(0, 0, 0, 0);
-    const float st = (float)srow[g];
-    const float zf = (float)zrow[g];
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    floatx4 aq = {0.0f, 0.0f, 0.0f, 0.0f}, as = {0.0f, 0.0f, 0.0f, 0.0f};
+      o.xv[j] = tok_ok ? *(const uint4*)(xrow + 128 * g + 8 * j) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // codes (c0, c4), (c1, c5), (c2, c6), (c3, c7) as exact fp16 pairs
-      const uint32_t p0 = sub_f16x2((w[j] & 0x000F000Fu) | kBias, kBias);
-      const uint32_t p1 = sub_f16x2(((w[j] >> 4) & 0x000F000Fu) | kBias, kBias);
-      const uint32_t p2 = sub_f16x2(((w[j] >> 8) & 0x000F000Fu) | kBias, kBias);
-      const uint32_t p3 = sub_f16x2(((w[j] >> 12) & 0x000F000Fu) | kBias, kBias);
-      const uint4 bv = make_uint4(lo_lo(p0, p1), lo_lo(p2, p3), hi_hi(p0, p1), hi_hi(p2, p3));
-      const half8 a = __builtin_bit_cast(half8, xv[j]);
-      const half8 b = __builtin_bit_cast(half8, bv);
-      aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, aq, 0, 0, 0);
-      as = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, as, 0, 0, 0);
+    for (int u = 0; u < kW4Tiles; ++u) o.q[u] = qrow[u][4 * g];
+  };
+  auto compute = [&](const Ops& o) {
+#pragma unroll
+    for (int u = 0; u < kW4Tiles; ++u) {
+      const uint32_t w[4] = {o.q[u].x, o.q[u].y, o.q[u].z, o.q[u].w};
+      floatx4 aq = {0.0f, 0.0f, 0.0f, 0.0f}, as = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // codes (c0, c4), (c1, c5), (c2, c6), (c3, c7) as exact fp16 pairs
+        const uint32_t p0 = sub_f16x2((w[j] & 0x000F000Fu) | kBias, kBias);
+        const uint32_t p1 = sub_f16x2(((w[j] >> 4) & 0x000F000Fu) | kBias, kBias);
+        const uint32_t p2 = sub_f16x2(((w[j] >> 8) & 0x000F000Fu) | kBias, kBias);
+        const uint32_t p3 = sub_f16x2(((w[j] >> 12) & 0x000F000Fu) | kBias, kBias);
+        const uint4 bv = make_uint4(lo_lo(p0, p1), lo_lo(p2, p3), hi_hi(p0, p1), hi_hi(p2, p3));
+        const half8 a = __builtin_bit_cast(half8, o.xv[j]);
+        const half8 b = __builtin_bit_cast(half8, bv);
+        aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, aq, 0, 0, 0);
+        if (u == 0) as = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, as, 0, 0, 0);
+      }
+      // the activation sums are the same for every row tile
+      if (u == 0) sum_x = as;
+      const float st = (float)o.st[u], zf = (float)o.zr[u];
+      // register r of lane l: token t0 + 4 (l / 16) + r, output row o0 + 16 u + l % 16
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[u][r] = fmaf(st, fmaf(-zf, sum_x[r], aq[r]), y[u][r]);
     }
-    // register r of lane l: token t0 + 4 (l / 16) + r, output row o0 + l % 16
-#pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = fmaf(st, fmaf(-zf, as[r], aq[r]), y[r]);
+  };
+  if (g0 < g1) {
+    Ops a, b;
+    load(a, g0);
+    int g = g0;
+    for (;;) {
+      load(b, g + 1);
+      compute(a);
+      if (++g >= g1) break;
+      load(a, g + 1);
+      compute(b);
+      if (++g >= g1) break;
+    }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][lane * 4 + r] = y[r];
+  for (int u = 0; u < kW4Tiles; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][(16 * u + (lane & 15)) * 16 + 4 * (lane >> 4) + r] = y[u][r];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int e = threadIdx.x;
+  for (int e = threadIdx.x; e < kW4Rows * 16; e += kW4Slices * 64) {
     float s = 0.0f;
 #pragma unroll
     for (int w = 0; w < kW4Slices; ++w) s += red[w][e];
-    const int l = e >> 2, r = e & 3;
-    const int t = t0 + 4 * (l >> 4) + r, o = o0 + (l & 15);
+    const int o = o0 + e / 16, t = t0 + e % 16;
     if (t < M && o < OUT) Y[(size_t)t * OUT + o] = s;
   }
 }
@@ -347,7 +394,7 @@ hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const 
       launch_gemv_k<4>(Xh, (int)M, (int)K, (int)OUT, qw, st, zr, Y, stream);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((OUT + 15) / 16), (unsigned)((M + 15) / 16));
+  const dim3 grid((unsigned)((OUT + kW4Rows - 1) / kW4Rows), (unsigned)((M + 15) / 16));
   hipLaunchKernelGGL(k_w4a16, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K, (int)OUT,
                      qw, st, zr, Y);
   return hipGetLastError();
