@@ -63,9 +63,15 @@ def pack_bytes(spec, group=128):
 
 
 def source_digest():
+    """Digest of the grid kernel's code (search_grid.hip and awq_device.h with
+    comments and blank lines removed and lines stripped), so that a counter
+    summary stays valid across edits of comments only."""
     h = hashlib.sha256()
     for f in ("search_grid.hip", "awq_device.h"):
-        h.update(open(os.path.join(ROOT, "post_bit_weight_awq_amd", "csrc", f), "rb").read())
+        src = open(os.path.join(ROOT, "post_bit_weight_awq_amd", "csrc", f)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        h.update("\n".join(ln.strip() for ln in src.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -364,12 +364,14 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
 // phase one group multiplies and the other prepares, so on every SIMD one
 // wavefront's MFMAs run beside the other wavefront's VALU and LDS work:
 //   * preparing step r: produce the group's 64 rows of dW(r+1) (each
-//     wavefront one 8-column piece), read step r's B fragments and, for even
-//     r, its A fragments into registers;
-//   * multiplying step r: the MFMAs, and between their two halves the loads:
-//     for even r it first reads step r+1's A fragments and then refills its
-//     activation buffer with the next chunk; its weight load; its group's
-//     data for a later column group.
+//     wavefront one 8-column piece), with step r's B fragments and, for even
+//     r, its A fragments read into registers in batches between the pieces'
+//     weight pairs;
+//   * multiplying step r: the MFMAs, and between their two halves (on the
+//     256-token tile: among the second half's MFMAs) the loads: for even r it
+//     first reads step r+1's A fragments and then refills its activation
+//     buffer with the next chunk; its weight load; its group's data for a
+//     later column group.
 // Group 0 prepares step r in phase 2r-1 and multiplies it in phase 2r;
 // group 1 prepares it in phase 2r and multiplies it in phase 2r+1.  dW(j) is
 // complete after phase 2j-2 and first read in phase 2j-1 (two dW buffers).
@@ -380,7 +382,8 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
 //   * raw weights: a group's own 64 rows, ring of three chunks, each chunk
 //     issued four to five steps before its first use;
 //   * per-group parameters and scales: a group's own copy, two column groups
-//     in flight.
+//     in flight (four for groups of 32 columns), each loaded in the multiply
+//     phase of step GS*g - 3 for column group g of GS steps.
 // The loads are inline assembly, so the compiler does not wait for them
 // before every LDS read; at the end of each multiply phase a wavefront waits
 // for all of its loads except that phase's own.  Nothing else in the loop
