@@ -553,6 +553,9 @@ def main():
                 per[nm][li] += dt / args.steps
                 samples[nm][li].append(dt)
 
+    def med(xs):
+        return sorted(xs)[len(xs) // 2]
+
     F = [search_flops(L["spec"], cfg.n_grid) for L in layers]
     total_F = sum(F)
     value = total_F / (ms_per_step * 1e-3) / 1e12
@@ -565,14 +568,15 @@ def main():
             "shape": [spec.n_tokens, spec.in_features, spec.out_features],
             "best_idx": int(L["best"].item()),
             "ms": {nm: round(per[nm][li], 5) for nm in names},
-            "ms_median": {nm: round(sorted(samples[nm][li])[len(samples[nm][li]) // 2], 5)
-                          for nm in names},
+            "ms_median": {nm: round(med(samples[nm][li]), 5) for nm in names},
             "ms_min": {nm: round(min(samples[nm][li]), 5) for nm in names},
             "grid_tflops": round(F[li] / (per["grid"][li] * 1e-3) / 1e12, 2),
             "search_tflops": round(F[li] / ((per["prepare"][li] + per["grid"][li] +
                                              per["select"][li]) * 1e-3) / 1e12, 2),
-            "stats_gbs": round(stats_bytes(spec) / (per["stats"][li] * 1e-3) / 1e9, 1),
-            "pack_gbs": round(pack_bytes(spec, cfg.group_size) / (per["pack"][li] * 1e-3) / 1e9, 1),
+            # the few-microsecond stages from their median: one late sample moves a mean
+            "stats_gbs": round(stats_bytes(spec) / (med(samples["stats"][li]) * 1e-3) / 1e9, 1),
+            "pack_gbs": round(pack_bytes(spec, cfg.group_size) /
+                              (med(samples["pack"][li]) * 1e-3) / 1e9, 1),
         }
     traffic = traffic_from_profiles(cfgspec.workload)
     calib = load_calib()
