@@ -8,12 +8,13 @@
 //
 // HBM-bound at decode sizes: 0.5 byte of codes + 4/128 byte of step and zero
 // per weight, read once.  A block (the MFMA kernel, k_w4a16, for more than 4
-// tokens) owns 32 output rows, as two 16-row tiles, and 16 token rows; its 4
-// wavefronts split the groups of 128 columns evenly and their partial outputs
-// are added in LDS at the end (fixed order, no atomics).  The two row tiles
-// share each group's activation fragments (the activations are re-read per
-// block, so the tiles halve that traffic), and a wavefront requests the next
-// group's codes, activations, steps and zeros before this group's arithmetic.
+// tokens) owns 16 token rows and TILES 16-row output tiles (two, or four when
+// that still gives the chip enough blocks); its 4 wavefronts split the groups
+// of 128 columns evenly and their partial outputs are added in LDS at the end
+// (fixed order, no atomics).  The row tiles share each group's activation
+// fragments (the activations are re-read per block, so more tiles cut that
+// traffic), and a wavefront requests the next group's codes, activations,
+// steps and zeros before this group's arithmetic.
 //   * Lane l holds output row o0 + 16 u + l % 16 of tile u and the 32-column
 //     slice l / 16 of the current group: one 16-byte load of 32 codes.  Each of
 //     its four words feeds one v_mfma_f32_16x16x32_f16 as the B operand; lane
@@ -36,8 +37,6 @@
 namespace awq {
 
 constexpr int kW4Slices = 4;   // wavefronts per block, each a share of the groups
-constexpr int kW4Tiles = 2;    // 16-row output tiles per wavefront (sharing the activations)
-constexpr int kW4Rows = 16 * kW4Tiles;  // output rows per block
 
 __device__ __forceinline__ uint32_t lo_lo(uint32_t a, uint32_t b) {
   return (a & 0xffffu) | (b << 16);
@@ -46,10 +45,13 @@ __device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
+// kW4Tiles 16-row output tiles per wavefront (sharing the activations)
+template <int kW4Tiles>
 __global__ void __launch_bounds__(kW4Slices * 64)
 k_w4a16(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __restrict__ qw,
         const _Float16* __restrict__ step16, const _Float16* __restrict__ zero16,
         float* __restrict__ Y) {
+  constexpr int kW4Rows = 16 * kW4Tiles;  // output rows per block
   __shared__ float red[kW4Slices][kW4Rows * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int o0 = blockIdx.x * kW4Rows, t0 = blockIdx.y * 16;
@@ -394,9 +396,21 @@ hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const 
       launch_gemv_k<4>(Xh, (int)M, (int)K, (int)OUT, qw, st, zr, Y, stream);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)((OUT + kW4Rows - 1) / kW4Rows), (unsigned)((M + 15) / 16));
-  hipLaunchKernelGGL(k_w4a16, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K, (int)OUT,
-                     qw, st, zr, Y);
+  // four row tiles per block halve the activation re-reads again, but only
+  // pay while the grid still covers most of the chip's 256 compute units
+  // (13B block at 16 tokens: 26.3 and 47.2 us for qkv and gate/up against 29.8
+  // and 53.0 with two tiles; 25.0 and 53.2 against 17.1 and 35.5 for the
+  // 5120-row layers, whose 80 blocks leave most units idle)
+  const int64_t t_tiles = (M + 15) / 16;
+  if ((OUT + 63) / 64 * t_tiles >= 192) {
+    const dim3 grid((unsigned)((OUT + 63) / 64), (unsigned)t_tiles);
+    hipLaunchKernelGGL(k_w4a16<4>, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K,
+                       (int)OUT, qw, st, zr, Y);
+  } else {
+    const dim3 grid((unsigned)((OUT + 31) / 32), (unsigned)t_tiles);
+    hipLaunchKernelGGL(k_w4a16<2>, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K,
+                       (int)OUT, qw, st, zr, Y);
+  }
   return hipGetLastError();
 }
 
