@@ -407,6 +407,8 @@ hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const 
     hipLaunchKernelGGL(k_w4a16<4>, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K,
                        (int)OUT, qw, st, zr, Y);
   } else {
+    // (one tile per block, twice the blocks, was slower still on the 5120-row
+    // layers: 22.1 and 50.2 us, the activation re-reads doubling)
     const dim3 grid((unsigned)((OUT + 31) / 32), (unsigned)t_tiles);
     hipLaunchKernelGGL(k_w4a16<2>, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K,
                        (int)OUT, qw, st, zr, Y);
