@@ -201,9 +201,11 @@ int awq_pack(const void* W, const float* s, int64_t in_features, int64_t out_fea
  *   step16, zero16: [out_features, in_features/128] fp16, 2-byte aligned
  *   Y:       [n_tokens, out_features] fp32, written, 4-byte aligned
  *   in_features a positive multiple of 128; 1 <= n_tokens <= 1048560.
- * Built for decode: one block per 16 output rows and 16 tokens, so the
- * weights stream from HBM once when n_tokens <= 16 (HBM-bound at 0.53 byte
- * per weight); larger n_tokens re-read them once per 16 tokens.
+ * Built for decode: up to 4 tokens stream each row's codes once without the
+ * matrix units; more tokens run blocks of 16 tokens x 32 or 64 output rows
+ * on them.  Either way the weights stream from HBM once when n_tokens <= 16
+ * (HBM-bound at 0.53 byte per weight); larger n_tokens re-read them once per
+ * 16 tokens.
  * Errors: AWQ_ERR_INVALID_ARG for NULL or misaligned pointers and sizes out
  * of range (nothing is enqueued); AWQ_ERR_HIP for a launch failure.
  * Source: dev.to page, "What do you actually deploy" (4-bit weights, 16-bit
