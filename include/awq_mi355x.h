@@ -155,8 +155,8 @@ int awq_search_layer(const void* X, const void* W, const float* sal, int64_t n_t
  * awq_search_layer(...) equals awq_search_layer_stages(AWQ_STAGE_ALL, ...).
  * A stage reads what the earlier stages left in the workspace, so the stages of
  * one search must run in order, on one workspace, with the same arguments.
- *   AWQ_STAGE_PREPARE: scale table, per-group quantizer parameters of every
- *                      grid point, and the reference output X W^T
+ *   AWQ_STAGE_PREPARE: scale table and the per-group quantizer parameters of
+ *                      every grid point (no reference output is formed)
  *   AWQ_STAGE_GRID:    the fused quantize-dequantize + MFMA contraction +
  *                      squared-error kernel over all grid points
  *   AWQ_STAGE_SELECT:  losses, argmin and s_best */
