@@ -9,12 +9,14 @@
 // HBM-bound at decode sizes: 0.5 byte of codes + 4/128 byte of step and zero
 // per weight, read once.  A block (the MFMA kernel, k_w4a16, for more than 4
 // tokens) owns 16 token rows and TILES 16-row output tiles (two, or four when
-// that still gives the chip enough blocks); its 4 wavefronts split the groups
-// of 128 columns evenly and their partial outputs are added in LDS at the end
-// (fixed order, no atomics).  The row tiles share each group's activation
-// fragments (the activations are re-read per block, so more tiles cut that
-// traffic), and a wavefront requests the next group's codes, activations,
-// steps and zeros before this group's arithmetic.
+// that still gives the chip enough blocks); its 4 (or, on small grids, 8)
+// wavefronts split the groups of 128 columns evenly and their partial outputs
+// are added in LDS at the end (fixed order, no atomics).  The row tiles share
+// each group's activation fragments (the activations are re-read per block,
+// so more tiles cut that traffic); a wavefront reads a group's activations as
+// whole cache lines and turns them into fragments through LDS, and requests
+// the next group's codes, activations, steps and zeros before this group's
+// arithmetic.
 //   * Lane l holds output row o0 + 16 u + l % 16 of tile u and the 32-column
 //     slice l / 16 of the current group: one 16-byte load of 32 codes.  Each of
 //     its four words feeds one v_mfma_f32_16x16x32_f16 as the B operand; lane
@@ -36,7 +38,6 @@
 
 namespace awq {
 
-constexpr int kW4Slices = 4;   // wavefronts per block, each a share of the groups
 
 __device__ __forceinline__ uint32_t lo_lo(uint32_t a, uint32_t b) {
   return (a & 0xffffu) | (b << 16);
@@ -45,23 +46,36 @@ __device__ __forceinline__ uint32_t hi_hi(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
 
-// kW4Tiles 16-row output tiles per wavefront (sharing the activations)
-template <int kW4Tiles>
+// kW4Tiles 16-row output tiles per wavefront (sharing the activations);
+// kW4Slices wavefronts per block, each a share of the groups
+template <int kW4Tiles, int kW4Slices>
 __global__ void __launch_bounds__(kW4Slices * 64)
 k_w4a16(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __restrict__ qw,
         const _Float16* __restrict__ step16, const _Float16* __restrict__ zero16,
         float* __restrict__ Y) {
   constexpr int kW4Rows = 16 * kW4Tiles;  // output rows per block
   __shared__ float red[kW4Slices][kW4Rows * 16];
+  // each wavefront's copy of one group's activations, 16 tokens x 256 bytes,
+  // rows padded by 16 bytes so the fragment reads spread over the banks
+  constexpr int kXRow = 17;  // uint4 per row
+  __shared__ uint4 xs[kW4Slices][16 * kXRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int o0 = blockIdx.x * kW4Rows, t0 = blockIdx.y * 16;
   const int r16 = lane & 15, j4 = lane >> 4;
-  const int tok = t0 + r16;
-  const bool tok_ok = tok < M;
   const int ng = K >> 7;
   const int g0 = (int)((int64_t)wave * ng / kW4Slices);
   const int g1 = (int)((int64_t)(wave + 1) * ng / kW4Slices);
-  const _Float16* xrow = X + (size_t)(tok_ok ? tok : 0) * K + 32 * j4;
+  // activation loads cover whole lines: load i of lane l reads the 16-byte
+  // piece l % 16 of token 4 i + l / 16 of the group (4 tokens x 256 bytes per
+  // load); tokens past the end read token 0 and count as zero
+  const _Float16* xp[4];
+  bool xok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * i + j4;
+    xok[i] = t < M;
+    xp[i] = X + (size_t)(xok[i] ? t : 0) * K + 8 * r16;
+  }
   const uint4* qrow[kW4Tiles];
   const _Float16* srow[kW4Tiles];
   const _Float16* zrow[kW4Tiles];
@@ -84,7 +98,7 @@ k_w4a16(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __re
   // arithmetic (groups past the wavefront's range re-read its last group)
   struct Ops {
     uint4 q[kW4Tiles];
-    uint4 xv[4];
+    uint4 xr[4];
     _Float16 st[kW4Tiles], zr[kW4Tiles];
   };
   auto load = [&](Ops& o, int g) {
@@ -95,12 +109,26 @@ k_w4a16(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __re
       o.zr[u] = zrow[u][g];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o.xv[j] = tok_ok ? *(const uint4*)(xrow + 128 * g + 8 * j) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i)
+      o.xr[i] = xok[i] ? *(const uint4*)(xp[i] + 128 * g) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < kW4Tiles; ++u) o.q[u] = qrow[u][4 * g];
   };
   auto compute = [&](const Ops& o) {
+    // the group's activations through the wavefront's LDS copy into fragment
+    // order: lane l takes token l % 16, columns 32 (l / 16) + 8 j .. + 7.  A
+    // wavefront's LDS operations run in order; the empty asm statements keep
+    // the compiler from moving these accesses across one another.
+    uint4* xw = xs[wave];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xw[(4 * i + j4) * kXRow + r16] = o.xr[i];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    uint4 xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xv[j] = xw[r16 * kXRow + 4 * j4 + j];
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int u = 0; u < kW4Tiles; ++u) {
       const uint32_t w[4] = {o.q[u].x, o.q[u].y, o.q[u].z, o.q[u].w};
@@ -113,7 +141,7 @@ k_w4a16(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4* __re
         const uint32_t p2 = sub_f16x2(((w[j] >> 8) & 0x000F000Fu) | kBias, kBias);
         const uint32_t p3 = sub_f16x2(((w[j] >> 12) & 0x000F000Fu) | kBias, kBias);
         const uint4 bv = make_uint4(lo_lo(p0, p1), lo_lo(p2, p3), hi_hi(p0, p1), hi_hi(p2, p3));
-        const half8 a = __builtin_bit_cast(half8, o.xv[j]);
+        const half8 a = __builtin_bit_cast(half8, xv[j]);
         const half8 b = __builtin_bit_cast(half8, bv);
         aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, aq, 0, 0, 0);
         if (u == 0) as = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, as, 0, 0, 0);
@@ -404,13 +432,17 @@ hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const 
   const int64_t t_tiles = (M + 15) / 16;
   if ((OUT + 63) / 64 * t_tiles >= 192) {
     const dim3 grid((unsigned)((OUT + 63) / 64), (unsigned)t_tiles);
-    hipLaunchKernelGGL(k_w4a16<4>, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K,
+    hipLaunchKernelGGL((k_w4a16<4, 4>), grid, dim3(4 * 64), 0, stream, Xh, (int)M, (int)K,
                        (int)OUT, qw, st, zr, Y);
   } else {
-    // (one tile per block, twice the blocks, was slower still on the 5120-row
-    // layers: 22.1 and 50.2 us, the activation re-reads doubling)
+    // A grid this small holds few loads in flight, so its blocks take eight
+    // wavefronts, each a shorter chain of groups (5120-row layers: 14.9 and
+    // 31.0 us against 16.8 and 36.6 with four; sixteen measured no better,
+    // and eight on the four-tile grid were slower on gate/up).  One tile per
+    // block, twice the blocks, was slower still: 22.1 and 50.2 us, the
+    // activation re-reads doubling.
     const dim3 grid((unsigned)((OUT + 31) / 32), (unsigned)t_tiles);
-    hipLaunchKernelGGL(k_w4a16<2>, grid, dim3(kW4Slices * 64), 0, stream, Xh, (int)M, (int)K,
+    hipLaunchKernelGGL((k_w4a16<2, 8>), grid, dim3(8 * 64), 0, stream, Xh, (int)M, (int)K,
                        (int)OUT, qw, st, zr, Y);
   }
   return hipGetLastError();
