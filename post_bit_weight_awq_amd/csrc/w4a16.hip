@@ -204,11 +204,25 @@ k_w4a16_gemv(const _Float16* __restrict__ X, int M, int K, int OUT, const uint4*
   float* xsum = (float*)(lds + MT * n8);  // [MT][ns]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int waves = gridDim.x * (kGemvThreads / 64);
-  for (int e = tid; e < MT * n8; e += kGemvThreads) {
-    const int t = e / n8, c = e - t * n8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t < M) v = *(const uint4*)(X + (size_t)t * K + 8 * c);
-    lds[e] = make_uint4(lo_lo(v.x, v.z), hi_hi(v.x, v.z), lo_lo(v.y, v.w), hi_hi(v.y, v.w));
+  // a thread's staging loads are all requested before the first is stored
+  // (one round trip instead of one per load)
+  constexpr int kStage = 4;
+  for (int e0 = tid; e0 < MT * n8; e0 += kStage * kGemvThreads) {
+    uint4 v[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int e = e0 + u * kGemvThreads;
+      const int t = e / n8, c = e - t * n8;
+      v[u] = make_uint4(0, 0, 0, 0);
+      if (e < MT * n8 && t < M) v[u] = *(const uint4*)(X + (size_t)t * K + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int e = e0 + u * kGemvThreads;
+      if (e < MT * n8)
+        lds[e] = make_uint4(lo_lo(v[u].x, v[u].z), hi_hi(v[u].x, v[u].z), lo_lo(v[u].y, v[u].w),
+                            hi_hi(v[u].y, v[u].w));
+    }
   }
   __syncthreads();
   for (int e = tid; e < MT * ns; e += kGemvThreads) {
