@@ -444,10 +444,18 @@ hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const 
   // and 53.0 with two tiles; 25.0 and 53.2 against 17.1 and 35.5 for the
   // 5120-row layers, whose 80 blocks leave most units idle)
   const int64_t t_tiles = (M + 15) / 16;
-  if ((OUT + 63) / 64 * t_tiles >= 192) {
+  const int64_t blocks4 = (OUT + 63) / 64 * t_tiles;
+  if (blocks4 >= 192) {
+    // eight wavefronts while the four-tile grid is under 1.5 blocks per unit
+    // (qkv, 240 blocks: 23.6 against 24.6 us), four above (gate/up, 432
+    // blocks: 39.5 against 42.6)
     const dim3 grid((unsigned)((OUT + 63) / 64), (unsigned)t_tiles);
-    hipLaunchKernelGGL((k_w4a16<4, 4>), grid, dim3(4 * 64), 0, stream, Xh, (int)M, (int)K,
-                       (int)OUT, qw, st, zr, Y);
+    if (blocks4 < 384)
+      hipLaunchKernelGGL((k_w4a16<4, 8>), grid, dim3(8 * 64), 0, stream, Xh, (int)M, (int)K,
+                         (int)OUT, qw, st, zr, Y);
+    else
+      hipLaunchKernelGGL((k_w4a16<4, 4>), grid, dim3(4 * 64), 0, stream, Xh, (int)M, (int)K,
+                         (int)OUT, qw, st, zr, Y);
   } else {
     // A grid this small holds few loads in flight, so its blocks take eight
     // wavefronts, each a shorter chain of groups (5120-row layers: 14.9 and
