@@ -208,3 +208,16 @@ def test_select_top_validation(lib):
         == _lib.AWQ_ERR_INVALID_ARG
     assert f(ctypes.c_void_p(0x1000), 8, 1, ctypes.c_void_p(0x1004), None) \
         == _lib.AWQ_ERR_INVALID_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the path runs on one GPU: a multi-GPU request exits with a message
+    # before any device work
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
