@@ -518,3 +518,44 @@ def test_variant_full_size_sampled_tiles(awq, group, w_bit, zp):
         for i in (0, 7, 19):
             want = O.tile_sq_error(X, W, s_tab[i], inv_s[i], rows, cols, group, w_bit, zp)
             assert abs(part[i, ti, oi] - want) <= LOSS_RTOL * want, (ti, oi, i)
+
+
+@pytest.mark.gpu
+def test_hot_path_replays_in_a_hip_graph(awq):
+    # stats, the search (both grid launches of the 512-token layer), pack and
+    # both W4A16 kernels captured once and replayed with eager work between the
+    # replays: every replay equals the eager result bit for bit
+    _say("hip graph: stats + search + pack + w4a16, 512x4096 -> 4096")
+    _, X, W = synth.make_custom(512, 4096, 4096, seed=11)
+    Xd = torch.from_numpy(X).cuda()
+    Wd = torch.from_numpy(W).cuda()
+    xq = Xd[:16].contiguous()
+
+    def run():
+        sal = awq.awq_act_stats(Xd)
+        res = awq.awq_search_layer(Xd, Wd, sal)
+        q, st, z = awq.awq_pack(Wd, res.s_best)
+        y1 = awq.awq_w4a16_matmul(xq[:1], q, st, z)
+        y16 = awq.awq_w4a16_matmul(xq, q, st, z)
+        return sal, res.losses, res.best_idx, res.s_best, q, st, z, y1, y16
+
+    ref = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    for rep in range(3):
+        junk = torch.randn(1 << 20, device="cuda")
+        junk.mul_(2.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {rep}"
+    assert int(ref[2].item()) >= 0
