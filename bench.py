@@ -456,7 +456,7 @@ def main():
             "config": {"workload": "llama13b_block_decode_w4a16_tok1",
                        "layers": [list(x) for x in DECODE_LAYERS], "tokens": 1,
                        "cache": "MALL cleared before each measurement"},
-            "roofline": {"bound": "hbm", "kernel": "k_w4a16", "achieved": one["block_gbs"],
+            "roofline": {"bound": "hbm", "kernel": "k_w4a16_gemv", "achieved": one["block_gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(one["block_gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
             "by_tokens": res,
