@@ -387,7 +387,7 @@ static void launch_gemv(const _Float16* X, int M, int K, int OUT, const uint4* q
                      M, K, OUT, qw, st, zr, Y);
 }
 
-// SL = 16-byte code loads per lane per row, the smallest of 2, 3, 4, 6, 8 that
+// SL = 16-byte code loads per lane per row, the smallest of 2 to 8 that
 // covers the row (K <= 64 * SL * 32); RW rows per wavefront and pass, the
 // fewest (1, 2, 3 or 4; at most 3 for SL > 4, whose registers allow no more)
 // with which the resident blocks hold every row in one pass, else the most.
@@ -414,8 +414,12 @@ static void launch_gemv_k(const _Float16* X, int M, int K, int OUT, const uint4*
     launch_gemv_rw<MT, 3>(X, M, K, OUT, qw, st, zr, Y, stream);
   else if (sl <= 4)
     launch_gemv_rw<MT, 4>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else if (sl <= 5)
+    launch_gemv_rw<MT, 5>(X, M, K, OUT, qw, st, zr, Y, stream);
   else if (sl <= 6)
     launch_gemv_rw<MT, 6>(X, M, K, OUT, qw, st, zr, Y, stream);
+  else if (sl <= 7)
+    launch_gemv_rw<MT, 7>(X, M, K, OUT, qw, st, zr, Y, stream);
   else
     launch_gemv_rw<MT, 8>(X, M, K, OUT, qw, st, zr, Y, stream);
 }

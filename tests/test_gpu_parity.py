@@ -356,7 +356,8 @@ def _w4a16_check(awq, x, qw, st, zr):
 # wavefront runs several passes, loading the next pass's slices as it goes.
 W4_CASES = [(1, 4096, 4096), (3, 384, 17), (16, 128, 16), (17, 256, 33), (40, 5120, 300),
             (1, 13824, 64), (1, 12416, 4100), (1, 128, 20000), (2, 512, 40000), (2, 128, 1),
-            (16, 256, 12300), (33, 384, 4100), (16, 256, 8200), (16, 384, 24600)]
+            (16, 256, 12300), (33, 384, 4100), (16, 256, 8200), (16, 384, 24600),
+            (1, 9216, 700), (2, 10240, 129)]
 
 
 @pytest.mark.parametrize("m,k,o", W4_CASES)
