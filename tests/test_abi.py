@@ -221,3 +221,25 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_committed_grid_profiles_match_the_grid_source():
+    # every committed summary of the grid kernel names the digest of the code
+    # it was taken on; a kernel edit without new counters shows up here (and
+    # the benchmark then reports its traffic as null)
+    import glob
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_for_digest", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    digest = bench.source_digest()
+    paths = sorted(glob.glob(os.path.join(root, "profiles", "*.md")))
+    named = 0
+    for p in paths:
+        txt = open(p).read()
+        for m in re.finditer(r"(?:source digest[^:]*:\s*|source=)([0-9a-f]{16})", txt):
+            named += 1
+            assert m.group(1) == digest, os.path.basename(p)
+    assert named >= 3
+    assert bench.traffic_from_profiles("llama7b_q_proj_in4096_out4096_tok512") is not None
