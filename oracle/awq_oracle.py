@@ -66,18 +66,26 @@ def act_stats(X: np.ndarray) -> np.ndarray:
     [P1] channel_importance listing (abs, then mean over the token axis);
     [P5] "Salient weight identification" (average absolute activation).
 
-    The sum is exact: |x| of an fp16 value is an integer multiple of 2^-24, so
-    summing those integers is exact for any token count.  The mean is then the
-    binary64 quotient, rounded to binary32.
+    The sum is exact: |x| of a finite fp16 value is an integer multiple of
+    2^-24, so summing those integers is exact for any token count.  The mean
+    is then the binary64 quotient, rounded to binary32.
+
+    Non-finite inputs follow IEEE addition of the |x| values: a channel with
+    a NaN has saliency NaN, otherwise a channel with an infinity has +inf.
     """
     X = np.asarray(X)
     if X.dtype != F16 or X.ndim != 2:
         raise TypeError("X must be a 2-D float16 array [tokens, in_features]")
     n = X.shape[0]
-    units = (np.abs(X).astype(F64) * 2.0 ** 24).astype(np.int64)   # exact integers
-    total = units.sum(axis=0, dtype=np.int64)                      # exact
-    mean = total.astype(F64) * 2.0 ** -24 / F64(n)
-    return mean.astype(F32)
+    a = np.abs(X).astype(F64)
+    finite = np.isfinite(a)
+    units = (np.where(finite, a, 0.0) * 2.0 ** 24).astype(np.int64)  # exact integers
+    total = units.sum(axis=0, dtype=np.int64)                        # exact
+    mean = (total.astype(F64) * 2.0 ** -24 / F64(n)).astype(F32)
+    has_inf = np.isinf(a).any(axis=0)
+    has_nan = np.isnan(a).any(axis=0)
+    mean = np.where(has_inf, F32(np.inf), mean)
+    return np.where(has_nan, F32(np.nan), mean).astype(F32)
 
 
 # --------------------------------------------------------------------------
@@ -111,11 +119,17 @@ class GroupQuant:
     step: np.ndarray   # [rows, n_groups] float32
     zero: np.ndarray   # [rows, n_groups] float32 (an integer value, +0 for zero)
     q: np.ndarray      # [rows, in] uint8 codes in 0 .. 2^b-1
-    tie: np.ndarray    # [rows, in] bool: pre-round value within 1 ulp of a .5 tie
+    tie: np.ndarray    # [rows, in] bool: the code's pre-round value, or its
+                       # group's zero-point pre-round value, within 1 ulp of a .5 tie
+    zero_tie: Optional[np.ndarray] = None  # [rows, n_groups] bool: the zero's pre-round
+                                           # value within 1 ulp of a .5 tie
 
 
 def _near_half(x: np.ndarray) -> np.ndarray:
-    """True where x lies within one binary32 ulp of a half-integer."""
+    """True where the binary32 value x lies within one binary32 ulp of x of a
+    half-integer (a value round-half-to-even could send either way once the
+    quotient before it is off by an ulp).  Where every binary32 value is an
+    integer (|x| >= 2^23) that holds for every x."""
     frac = np.abs(x.astype(F64) - (np.floor(x.astype(F64)) + 0.5))
     return frac <= np.spacing(np.abs(x).astype(F32)).astype(F64)
 
@@ -159,9 +173,10 @@ def quantize(ws: np.ndarray, group: int = GROUP, w_bit: int = W_BIT,
         zero = np.full_like(step, F32(2 ** (w_bit - 1)))
     x = (g / step[:, :, None]).astype(F32)
     q = np.clip(np.rint(x) + zero[:, :, None], F32(0), qmax).astype(F32)
-    tie = _near_half(x) | (_near_half(zpre)[:, :, None] if zero_point else False)
+    zero_tie = _near_half(zpre) if zero_point else np.zeros(zpre.shape, dtype=bool)
+    tie = _near_half(x) | zero_tie[:, :, None]
     return GroupQuant(step, zero, q.reshape(rows, k).astype(np.uint8),
-                      tie.reshape(rows, k))
+                      tie.reshape(rows, k), zero_tie)
 
 
 def scaled_weights(W: np.ndarray, s_row: np.ndarray) -> np.ndarray:
@@ -249,18 +264,33 @@ class SearchResult:
 
 def search_layer(X: np.ndarray, W: np.ndarray, sal: np.ndarray, n_grid: int = N_GRID,
                  floor: float = SAL_FLOOR, group: int = GROUP, w_bit: int = W_BIT,
-                 zero_point: bool = True) -> SearchResult:
+                 zero_point: bool = True, row_chunk: Optional[int] = None) -> SearchResult:
     """The per-layer grid search, in the order of [P1]'s search_scale listing:
     reference output; for each alpha: scale, quantize, fold back, output MSE;
-    keep the first strict minimum."""
+    keep the first strict minimum.
+
+    ``row_chunk`` runs the same steps on blocks of that many output rows at a
+    time and adds each block's sum of squared differences (the quantizer
+    works row by row, so a block's codes are those of the whole layer); the
+    loss is the total over all N * out outputs divided by their count.  It
+    only bounds the memory the large layers need; without it the layer is one
+    block."""
     s, inv_s = scale_table(sal, n_grid, floor)
     X64 = np.asarray(X, F16).astype(F64)
-    y_ref = X64 @ np.asarray(W, F16).astype(F64).T
-    losses = np.empty(n_grid, dtype=F64)
-    for i in range(n_grid):
-        wq = fake_quant(W, s[i], inv_s[i], group, w_bit, zero_point)
-        d = X64 @ wq.astype(F64).T - y_ref
-        losses[i] = np.mean(d * d)
+    W = np.asarray(W, F16)
+    n_out = W.shape[0]
+    chunk = n_out if row_chunk is None else int(row_chunk)
+    if chunk <= 0:
+        raise ValueError("row_chunk must be positive")
+    sums = np.zeros(n_grid, dtype=F64)
+    for o0 in range(0, n_out, chunk):
+        Wc = W[o0:o0 + chunk]
+        y_ref = X64 @ Wc.astype(F64).T
+        for i in range(n_grid):
+            wq = fake_quant(Wc, s[i], inv_s[i], group, w_bit, zero_point)
+            d = X64 @ wq.astype(F64).T - y_ref
+            sums[i] += np.sum(d * d)
+    losses = sums / F64(X64.shape[0] * n_out)
     best = argmin_first(losses)
     return SearchResult(losses, best, s[best].copy(), s, inv_s)
 
@@ -290,7 +320,8 @@ class Packed:
     step16: np.ndarray    # [out, in/group] float16
     zero16: np.ndarray    # [out, in/group] float16
     q: np.ndarray         # [out, in] uint8 (unpacked codes)
-    tie: np.ndarray       # [out, in] bool
+    tie: np.ndarray       # [out, in] bool (see GroupQuant.tie)
+    zero_tie: np.ndarray  # [out, in/group] bool (see GroupQuant.zero_tie)
 
 
 def pack_codes(q: np.ndarray) -> np.ndarray:
@@ -322,7 +353,8 @@ def pack(W: np.ndarray, s_row: np.ndarray, group: int = GROUP, w_bit: int = W_BI
     [P3] worked example: one 16-bit scale per 128 weights).  Codes of fewer
     than 4 bits still take one nibble each."""
     gq = quantize(scaled_weights(W, s_row), group, w_bit, zero_point)
-    return Packed(pack_codes(gq.q), gq.step.astype(F16), gq.zero.astype(F16), gq.q, gq.tie)
+    return Packed(pack_codes(gq.q), gq.step.astype(F16), gq.zero.astype(F16), gq.q, gq.tie,
+                  gq.zero_tie)
 
 
 def packed_bytes(n_weights: int, group: int = GROUP, w_bit: int = W_BIT) -> dict:

@@ -571,9 +571,126 @@ def test_literal_division_changes_loss_negligibly():
         assert abs(a - b) <= 1e-5 * a
 
 
+# ------------------------------------------------ the .5-tie flags of codes
+def _f32_steps(x, n):
+    """x moved by n binary32 ulps (n < 0: towards -inf)."""
+    v = np.float32(x)
+    d = np.float32(np.inf if n > 0 else -np.inf)
+    for _ in range(abs(n)):
+        v = np.nextafter(v, d)
+    return v
+
+
+NEAR_HALF_CASES = [
+    # (value, within one ulp of x of a half-integer?)
+    (2.5, True), (_f32_steps(2.5, 1), True), (_f32_steps(2.5, -1), True),
+    (_f32_steps(2.5, 2), False), (_f32_steps(2.5, -2), False),
+    (3.0, False), (2.0, False), (0.0, False), (0.5, True), (_f32_steps(0.5, 3), False),
+    (-2.5, True), (_f32_steps(-2.5, 1), True), (_f32_steps(-2.5, -1), True),
+    (-3.25, False), (14.5, True), (_f32_steps(14.5, -1), True), (_f32_steps(14.5, 2), False),
+    # ulp 0.25 in [2^21, 2^22): an integer is two ulps from a half-integer, a
+    # quarter one ulp; ulp 0.5 in [2^22, 2^23): every value is a tie or one ulp from one
+    (2097152.0, False), (2097152.25, True), (2097153.75, True),
+    (4194304.5, True), (4194305.0, True), (4194306.0, True),
+    # every binary32 value at or beyond 2^23 is an integer, 0.5 from a half-integer, ulp >= 1
+    (8388609.0, True), (-16777218.0, True),
+]
+
+
+@pytest.mark.parametrize("x,want", NEAR_HALF_CASES)
+def test_near_half_hand_values(x, want):
+    """The tie flag counts the codes whose pre-round binary32 quotient lies
+    within one binary32 ulp of a half-integer (round-half-to-even, dev.to "Why
+    does naive 4-bit quantization wreck LLM accuracy?" round-to-nearest; the
+    quotient of the step-size equation of "AWQ > Salient Weight Preservation").
+    Expected values from the binary32 spacing at each value, worked by hand."""
+    got = O._near_half(np.array([x], dtype=F32))[0]
+    assert bool(got) == want, (float(x), float(np.spacing(np.float32(abs(x)))))
+
+
+def test_tie_flags_mark_codes_that_an_ulp_can_flip():
+    """On random groups, a code flagged as near a tie is exactly one whose
+    rounding changes when its quotient moves by one ulp either way (computed
+    with exact rationals), or whose group's zero point does; unflagged codes
+    never change."""
+    rng = np.random.default_rng(21)
+    ws = (rng.standard_normal((64, 256)) * 0.05).astype(F32)
+    # plant exact and near ties: groups whose quotient lands on x.5 by construction
+    ws[:8, :128] = ((np.arange(128) % 16 - 7.5) / 16).astype(F32)
+    gq = O.quantize(ws)
+    for r in range(ws.shape[0]):
+        for g in range(ws.shape[1] // 128):
+            step = Fraction(float(gq.step[r, g]))
+            for j in range(128):
+                x = brute.round_rne(Fraction(float(ws[r, 128 * g + j])) / step)
+                xf = np.float32(float(x))
+                ulp = Fraction(float(np.spacing(np.float32(abs(xf)))))
+                flips = {brute.rint_even(x - ulp), brute.rint_even(x), brute.rint_even(x + ulp)}
+                code_flag = bool(O._near_half(np.array([xf]))[0])
+                if len(flips) > 1:
+                    assert code_flag, (r, g, j, float(x))
+                if not (code_flag or gq.zero_tie[r, g]):
+                    assert not gq.tie[r, 128 * g + j]
+                assert gq.tie[r, 128 * g + j] == (code_flag or gq.zero_tie[r, g])
+    assert gq.tie[:8, :128].all()  # planted exact ties
+
+
+# ------------------------------------------------- non-finite activations
+def test_stats_non_finite_columns():
+    """A channel whose tokens hold a NaN has saliency NaN, one holding an
+    infinity (and no NaN) +inf (IEEE sums of |x|); the other channels keep
+    their exact mean, checked against exact rationals."""
+    rng = np.random.default_rng(22)
+    X = rng.standard_normal((37, 24)).astype(F16)
+    X[3, 1] = np.nan
+    X[5, 2] = np.inf
+    X[6, 3] = -np.inf
+    X[7, 4] = np.nan
+    X[8, 4] = np.inf
+    sal = O.act_stats(X)
+    assert np.isnan(sal[1]) and np.isnan(sal[4])
+    assert sal[2] == np.inf and sal[3] == np.inf
+    for k in [0] + list(range(5, 24)):
+        exact = brute.mean_abs_exact([Fraction(float(v)) for v in X[:, k]])
+        assert sal[k] == np.float32(float(brute.round_rne(brute.round_rne(exact, brute.BINARY64))))
+
+
+# --------------------------------------- the W4A16 error-bound scale
+def test_w4a16_abs_matmul_matches_exact_rationals_and_bounds_the_product():
+    """sum_k |x| (q + |z|) |step| against exact rationals with an independent
+    bit-level unpack, and as a bound of |x (q - z) step| (triangle inequality)
+    that is attained when x >= 0 and the zeros are <= 0."""
+    rng = np.random.default_rng(23)
+    rows, k, m = 3, 256, 2
+    qw, st, zr = _random_packed(rng, rows, k)
+    zr[1, 0] = F16(-7.0)
+    st[2, 1] = F16(-0.03125)
+    x = rng.standard_normal((m, k)).astype(F16)
+    b = O.w4a16_abs_matmul(x, qw, st, zr)
+    for t in range(m):
+        for o in range(rows):
+            acc = Fraction(0)
+            for col in range(k):
+                word = int(qw.view(np.uint32)[o, col // 8])
+                code = (word >> (4 * (col % 8))) & 0xF
+                g = col // 128
+                acc += abs(Fraction(float(x[t, col]))) * (code + abs(Fraction(float(zr[o, g])))) \
+                    * abs(Fraction(float(st[o, g])))
+            assert b[t, o] == pytest.approx(float(acc), rel=1e-12, abs=1e-300)
+    y = O.w4a16_matmul(x, qw, st, zr)
+    assert np.all(np.abs(y) <= b * (1 + 1e-12))
+    xp = np.abs(x)
+    zn = -np.abs(zr)
+    stp = np.abs(st)
+    assert np.allclose(O.w4a16_matmul(xp, qw, stp, zn), O.w4a16_abs_matmul(xp, qw, stp, zn),
+                       rtol=1e-12, atol=0)
+
+
 # ------------------------------------------- planted mistakes must be caught
 @pytest.mark.parametrize("mutation", ["floor_round", "symmetric_step", "grid_to_one",
-                                      "no_zero_canon", "nibble_order", "fold_multiplies"])
+                                      "no_zero_canon", "nibble_order", "fold_multiplies",
+                                      "abs_bound_drops_zero", "tie_exact_only",
+                                      "stats_nan_ignored"])
 def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
     """Each plausible slip in the oracle trips at least one pin above."""
     if mutation == "floor_round":
@@ -612,6 +729,24 @@ def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
                                             ).astype(F16))
         with pytest.raises(AssertionError):
             test_fold_into_rmsnorm_preserves_the_layer()
+    elif mutation == "abs_bound_drops_zero":
+        def no_zero(x, qweight, step16, zero16, group=128):
+            q = O.unpack_codes(qweight).astype(F64)
+            st = np.abs(np.repeat(np.asarray(step16, F16).astype(F64), group, axis=1))
+            return np.abs(np.asarray(x, F16).astype(F64)) @ (q * st).T
+        monkeypatch.setattr(O, "w4a16_abs_matmul", no_zero)
+        with pytest.raises(AssertionError):
+            test_w4a16_abs_matmul_matches_exact_rationals_and_bounds_the_product()
+    elif mutation == "tie_exact_only":
+        monkeypatch.setattr(O, "_near_half", lambda x: np.abs(
+            x.astype(F64) - (np.floor(x.astype(F64)) + 0.5)) == 0)
+        with pytest.raises(AssertionError):
+            test_near_half_hand_values(_f32_steps(2.5, 1), True)
+    elif mutation == "stats_nan_ignored":
+        orig = O.act_stats
+        monkeypatch.setattr(O, "act_stats", lambda X: orig(np.where(np.isnan(X), F16(0), X)))
+        with pytest.raises(AssertionError):
+            test_stats_non_finite_columns()
     elif mutation == "no_zero_canon":
         orig = O.quantize
 
