@@ -101,9 +101,16 @@ const char* awq_version(void);
  *   X:        [n_tokens, in_features] fp16, read only
  *   sal_out:  [in_features] fp32, written
  *   n_tokens >= 1, in_features >= 8 and a multiple of 8.
- * The workspace holds per-row-chunk partial column sums (64-bit integers):
- * between 8 * in_features and 8 * in_features * (1 + n_tokens / 64) bytes.
- * Its contents on entry do not matter.
+ * Non-finite inputs follow IEEE sums of the magnitudes: a channel with a NaN
+ * gets NaN, else a channel with an infinity gets +inf.
+ * The call takes a caller workspace, unlike a plain (X, n_tokens,
+ * in_features, sal_out, stream) form, on purpose: the column sums of a large
+ * X are split over many blocks, and the workspace holds their exact per-row-
+ * chunk partials (64-bit integers) so the total is exact and bit-for-bit
+ * deterministic with no atomics and no memory held by the library.  Size:
+ * between 8 * in_features and 8 * in_features * (1 + n_tokens / 64) bytes
+ * (none is used when n_tokens <= 8192 and n_tokens * in_features <= 2^22: one
+ * launch then reads all of X).  Its contents on entry do not matter.
  * Source: dev.to page, channel_importance listing; Summary page,
  * "Salient weight identification".
  * ---------------------------------------------------------------------- */
@@ -117,8 +124,12 @@ int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* s
  *   W:            [out_features, in_features] fp16 (fused layers: rows concatenated)
  *   sal:          [in_features] fp32 (from awq_act_stats or any source)
  *   losses_out:   [n_grid] float64: L_i, the mean squared output error
- *   best_idx_out: [1] int32: i*, or -1 when no L_i is finite
+ *   best_idx_out: [1] int32: i*, or -1 when no L_i is finite (the outcome
+ *                 AWQ_ERR_NONFINITE names; a caller reads it after the stream
+ *                 has reached the call, since the call itself only enqueues)
  *   s_best_out:   [in_features] fp32: s_i* (all NaN when i* = -1)
+ *   A NaN or infinite sal_k gives s = 1 at alpha = 0 and NaN or inf above it
+ *   (the floor keeps a NaN), so every grid point above 0 has a NaN loss.
  *   in_features must be a multiple of 128; n_tokens, out_features >= 1.
  * The workspace (size from awq_search_workspace_size) holds the scale table,
  * the per-group quantizer parameters and the per-tile partial sums;

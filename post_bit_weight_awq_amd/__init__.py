@@ -12,6 +12,7 @@ the built library the calls raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from dataclasses import dataclass
 from typing import Optional
@@ -48,6 +49,13 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Context in which the binding allocates its outputs and workspaces: the
+    stream the kernels run on, so torch's caching allocator hands the memory
+    to no other stream while they may still be pending."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -76,11 +84,12 @@ def awq_act_stats(X: torch.Tensor, *, out: Optional[torch.Tensor] = None,
     if X.dim() != 2:
         raise ValueError("X must be [tokens, in_features]")
     n, k = X.shape
-    if out is None:
-        out = torch.empty(k, dtype=torch.float32, device=X.device)
-    if workspace is None:
-        workspace = torch.empty(awq_act_stats_workspace_size(n, k), dtype=torch.uint8,
-                                device=X.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(k, dtype=torch.float32, device=X.device)
+        if workspace is None:
+            workspace = torch.empty(awq_act_stats_workspace_size(n, k), dtype=torch.uint8,
+                                    device=X.device)
     check(load().awq_act_stats(
         ctypes.c_void_p(_dev(X, "X", torch.float16, (n, k))), n, k,
         ctypes.c_void_p(_dev(out, "out", torch.float32, (k,))),
@@ -138,14 +147,15 @@ def awq_search_layer(X: torch.Tensor, W: torch.Tensor, sal: torch.Tensor,
     o = W.shape[0]
     plan = awq_search_plan(n, k, o, cfg)
     dev = X.device
-    if workspace is None:
-        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
-    if losses is None:
-        losses = torch.empty(cfg.n_grid, dtype=torch.float64, device=dev)
-    if best_idx is None:
-        best_idx = torch.empty(1, dtype=torch.int32, device=dev)
-    if s_best is None:
-        s_best = torch.empty(k, dtype=torch.float32, device=dev)
+    with _on(stream):
+        if workspace is None:
+            workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
+        if losses is None:
+            losses = torch.empty(cfg.n_grid, dtype=torch.float64, device=dev)
+        if best_idx is None:
+            best_idx = torch.empty(1, dtype=torch.int32, device=dev)
+        if s_best is None:
+            s_best = torch.empty(k, dtype=torch.float32, device=dev)
     check(load().awq_search_layer_stages(
         stages, ctypes.c_void_p(_dev(X, "X", torch.float16, (n, k))),
         ctypes.c_void_p(_dev(W, "W", torch.float16, (o, k))),
@@ -172,12 +182,13 @@ def awq_pack(W: torch.Tensor, s: torch.Tensor, cfg: Optional[AwqConfig] = None, 
     dev = W.device
     if k % 8 or k % g:
         raise ValueError(f"in_features={k} must be a multiple of {g}")
-    if qweight is None:
-        qweight = torch.empty((o, k // 8), dtype=torch.int32, device=dev)
-    if step is None:
-        step = torch.empty((o, k // g), dtype=torch.float16, device=dev)
-    if zero is None:
-        zero = torch.empty((o, k // g), dtype=torch.float16, device=dev)
+    with _on(stream):
+        if qweight is None:
+            qweight = torch.empty((o, k // 8), dtype=torch.int32, device=dev)
+        if step is None:
+            step = torch.empty((o, k // g), dtype=torch.float16, device=dev)
+        if zero is None:
+            zero = torch.empty((o, k // g), dtype=torch.float16, device=dev)
     check(load().awq_pack(
         ctypes.c_void_p(_dev(W, "W", torch.float16, (o, k))),
         ctypes.c_void_p(_dev(s, "s", torch.float32, (k,))), k, o, ctypes.byref(cfg),
@@ -198,8 +209,9 @@ def awq_w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, step: torch.Tensor,
     o = qweight.shape[0]
     if k % 128:
         raise ValueError(f"in_features={k} must be a multiple of 128")
-    if out is None:
-        out = torch.empty((n, o), dtype=torch.float32, device=X.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((n, o), dtype=torch.float32, device=X.device)
     check(load().awq_w4a16_matmul(
         ctypes.c_void_p(_dev(X, "X", torch.float16, (n, k))), n, k, o,
         ctypes.c_void_p(_dev(qweight, "qweight", torch.int32, (o, k // 8))),
@@ -219,8 +231,9 @@ def awq_fold_inverse_scale(src: torch.Tensor, s: torch.Tensor, *,
         raise ValueError("src must be [n] or [n, cols]")
     rows = src.shape[0]
     cols = 1 if src.dim() == 1 else src.shape[1]
-    if out is None:
-        out = torch.empty_like(src)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(src)
     check(load().awq_fold_inverse_scale(
         ctypes.c_void_p(_dev(src, "src", torch.float16, tuple(src.shape))),
         ctypes.c_void_p(_dev(s, "s", torch.float32, (rows,))), rows, cols,
@@ -241,8 +254,9 @@ def awq_select_top_channels(sal: torch.Tensor, n_keep: int, *,
     if sal.dim() != 1:
         raise ValueError("sal must be [in_features]")
     n = sal.shape[0]
-    if out is None:
-        out = torch.empty_like(sal)
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(sal)
     check(load().awq_select_top_channels(
         ctypes.c_void_p(_dev(sal, "sal", torch.float32, (n,))), n, int(n_keep),
         ctypes.c_void_p(_dev(out, "out", torch.float32, (n,))), _stream(stream)))

@@ -12,6 +12,10 @@
 // integers in units of 2^-24, one row of partials per chunk.  A second kernel
 // adds each column's partials (integer adds: exact, in a fixed order) and
 // divides once.  Two launches, no atomics, no state kept between calls.
+// Non-finite inputs follow IEEE sums of |x|: a column holding a NaN gets NaN,
+// else one holding an infinity +inf.  The partials carry them as the two
+// largest 64-bit values, which no finite column sum reaches (at most
+// 2^24 tokens x 65504 x 2^24 < 2^64 - 2).
 // Inputs of at most 4M elements take one launch instead (k_act_stats_1p): the
 // whole input is then in flight at once, and a second launch would cost more
 // than the parallelism it adds (measured 8.8 -> 6.4 us on 512 x 4096; on
@@ -20,6 +24,9 @@
 #include "awq_internal.h"
 
 namespace awq {
+
+constexpr unsigned long long kPartInf = ~0ull - 1;  // some term was +inf, none NaN
+constexpr unsigned long long kPartNaN = ~0ull;      // some term was NaN
 
 constexpr int kStatsThreads = 256;
 constexpr int kStatsCols = kWave * 8;  // columns per block
@@ -75,7 +82,8 @@ k_act_stats(const uint4* __restrict__ X, int64_t n_tokens, int64_t in_features,
     const int64_t gc = (int64_t)blockIdx.x * kStatsCols + c;
     if (gc < in_features) {
       const double t = red[0][c] + red[1][c] + red[2][c] + red[3][c];
-      prow[gc] = (unsigned long long)(t * 16777216.0);  // exact: t is a multiple of 2^-24
+      // exact: a finite t is a multiple of 2^-24
+      prow[gc] = t != t ? kPartNaN : t == INFINITY ? kPartInf : (unsigned long long)(t * 16777216.0);
     }
   }
 }
@@ -87,21 +95,33 @@ __global__ void __launch_bounds__(1024)
 k_stats_finalize(const unsigned long long* __restrict__ part, int64_t row_chunks,
                  int64_t in_features, int64_t n_tokens, float* __restrict__ sal) {
   __shared__ unsigned long long sh[16][64];
+  __shared__ unsigned long long shf[16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t k = (int64_t)blockIdx.x * 64 + lane;
-  unsigned long long acc = 0;
+  unsigned long long acc = 0, flag = 0;  // flag: the largest non-finite code seen
   if (k < in_features)
-    for (int64_t c = wave; c < row_chunks; c += 16) acc += part[c * in_features + k];
+    for (int64_t c = wave; c < row_chunks; c += 16) {
+      const unsigned long long v = part[c * in_features + k];
+      if (v >= kPartInf)
+        flag = v > flag ? v : flag;
+      else
+        acc += v;
+    }
   sh[wave][lane] = acc;
+  shf[wave][lane] = flag;
   __syncthreads();
   if (wave == 0 && k < in_features) {
-    unsigned long long tot = 0;
+    unsigned long long tot = 0, fl = 0;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) tot += sh[w][lane];
+    for (int w = 0; w < 16; ++w) {
+      tot += sh[w][lane];
+      fl = shf[w][lane] > fl ? shf[w][lane] : fl;
+    }
     // binary64 value of the exact sum (rounded only beyond 2^53 units), then
     // the binary64 quotient, then binary32.
     const double total = (double)tot * 0x1p-24;
-    sal[k] = (float)(total / (double)n_tokens);
+    sal[k] = fl == kPartNaN ? __builtin_nanf("") : fl == kPartInf ? INFINITY
+                                                                  : (float)(total / (double)n_tokens);
   }
 }
 

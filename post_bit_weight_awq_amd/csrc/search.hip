@@ -34,7 +34,8 @@ k_scale_table(const float* __restrict__ sal, float* __restrict__ s_tab,
   const int i = (int)(idx / K);
   const int64_t k = idx - (int64_t)i * K;
   const float v = sal[k];
-  const double base = (double)(v > floor_v ? v : floor_v);
+  // the floor as a maximum that keeps a NaN saliency (pow(NaN, 0) is still 1)
+  const double base = (double)(v < floor_v ? floor_v : v);
   const double alpha = (double)i / (double)n_grid;
   const float s = (float)pow(base, alpha);
   s_tab[idx] = s;

@@ -430,9 +430,11 @@ hipError_t launch_w4a16(const void* X, int64_t M, int64_t K, int64_t OUT, const 
   const uint4* qw = (const uint4*)qweight;
   const _Float16* st = (const _Float16*)step16;
   const _Float16* zr = (const _Float16*)zero16;
-  // the streaming kernel keeps a row's codes in registers (K <= 16384) and the
-  // activations in LDS (at most 64 KiB)
-  const bool gemv_fits = K <= 64 * 8 * 32 && M <= 4 && (size_t)M * K * 2 <= 65536;
+  // the streaming kernel keeps a row's codes in registers (K <= 16384) and its
+  // MT staged token rows (1, 2, or 4 for 3 and 4 tokens) with their slice sums
+  // in at most 64 KiB of LDS
+  const int mt = M == 1 ? 1 : M == 2 ? 2 : 4;
+  const bool gemv_fits = K <= 64 * 8 * 32 && M <= 4 && gemv_lds(mt, (int)K) <= 65536;
   if (gemv_fits) {
     if (M == 1)
       launch_gemv_k<1>(Xh, (int)M, (int)K, (int)OUT, qw, st, zr, Y, stream);
