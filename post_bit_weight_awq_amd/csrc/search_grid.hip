@@ -15,18 +15,16 @@
 //
 // Two kernels share this file.  k_grid_pp (after k_grid) runs the 512- and
 // 256-token tiles, for groups of 32, 64 and 128 columns; k_grid runs the
-// 128-token tile.  The notes below describe k_grid; those of k_grid_pp stand
-// above it.
+// 128-token tile (the whole tile of small layers, and the halves of a split
+// 256-token round).  The notes below describe k_grid; those of k_grid_pp
+// stand above it.
 //
 // Layout (BM tokens x BN outputs per block, NW wavefronts, K steps of 32):
-//   * NW wavefronts stacked along tokens (8 for the 512- and 256-token tiles,
-//     two per SIMD, so one wavefront's loads and weight production overlap the
-//     other's MFMAs); each owns BM/NW tokens x BN outputs as 16x16 tiles of
-//     v_mfma_f32_16x16x32_f16, whose fp32 accumulators stay in registers for
-//     the whole K loop.
+//   * NW = 4 wavefronts stacked along tokens, one per SIMD; each owns BM/NW
+//     tokens x BN outputs as 16x16 tiles of v_mfma_f32_16x16x32_f16, whose
+//     fp32 accumulators stay in registers for the whole K loop.
 //   * Activations go from global memory straight into each wavefront's
-//     A-fragment registers, one K step ahead (the other wavefront on the SIMD
-//     covers the latency).  The 16x16x32 fragment is 16
+//     A-fragment registers, one K step ahead.  The 16x16x32 fragment is 16
 //     rows x 64 contiguous bytes, so each load instruction touches 16 cache
 //     sectors: half as many as a 32x32 fragment, which matters because the
 //     vector data-return path, not bandwidth, limits these loads.
@@ -65,6 +63,7 @@
 
 #include "awq_device.h"
 #include "awq_internal.h"
+#include "grid_index.h"
 
 namespace awq {
 
@@ -88,19 +87,15 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   __shared__ __attribute__((aligned(16))) float scl[2][2 * KC];       // s | 1/s of a step
   __shared__ double red[NW];
 
+  static_assert(BN == 128, "the unit mapping assumes 128-row output tiles");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_tiles = n_t_tiles * n_o_tiles;
-  // unit u and token half h: whole tiles take one block per unit; halves take
-  // blocks b and b + 8 (same XCD) for the two halves of unit base + b%8 + 8(b/16)
-  const int b = blockIdx.x;
-  const int u = unit_base + (split == 1 ? b : (b & 7) + 8 * (b >> 4));
-  const int h = split == 1 ? 0 : (b >> 3) & 1;
-  const int jb = u >> 3;
-  const int ai = jb % n_grid;
-  const int T = (jb / n_grid) * 8 + (u & 7);
+  // unit and token half of this block (whole tiles: one block per unit)
+  const gidx::Unit un =
+      gidx::unit_of_block(blockIdx.x, unit_base, split, n_grid, n_o_tiles, BM);
+  const int ai = un.ai, T = un.T, h = un.h;
   if (T >= n_tiles) return;
-  const int tt = T / n_o_tiles, ot = T - tt * n_o_tiles;
-  const int t0 = tt * BM * split + h * BM, o0 = ot * BN;
+  const int t0 = un.t0, o0 = un.o0;
   if (t0 >= N) {  // second half of a ragged last token tile: no rows
     if (threadIdx.x == 0) partials[2 * ((size_t)ai * n_tiles + T) + h] = 0.0;
     return;
@@ -115,19 +110,13 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   const _Float16* xt = X + (size_t)t0 * K;
   uint32_t pa[MBW];
 #pragma unroll
-  for (int m = 0; m < MBW; ++m) {
-    const int row = min(t0 + wave * WMT + m * 16 + (lane & 15), N - 1) - t0;
-    pa[m] = (uint32_t)row * (uint32_t)K + 8 * (lane >> 4);
-  }
+  for (int m = 0; m < MBW; ++m) pa[m] = gidx::g_act_offset(t0, N, K, wave, WMT, m, lane);
   // coalesced raw-weight loads: thread t covers 16 bytes of row t/4 (+ NT/4 j),
   // as 32-bit offsets from the tile's first row
   const _Float16* wt = W + (size_t)o0 * K;
   uint32_t pwl[PR];
 #pragma unroll
-  for (int j = 0; j < PR; ++j) {
-    const int go = min(o0 + (tid >> 2) + (NT / 4) * j, OUT - 1) - o0;
-    pwl[j] = (uint32_t)go * (uint32_t)K + 8 * (tid & 3);
-  }
+  for (int j = 0; j < PR; ++j) pwl[j] = gidx::g_w_offset(o0, OUT, K, tid, NT, j);
   // production: the wavefront-uniform chunk pc of rows prow0 + (NT/4) j
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int pc = wv & 3;
@@ -136,7 +125,7 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   const GroupParams* pt = prm + (size_t)ai * ngroups * OUT + o0;
   uint32_t pp[PR];
 #pragma unroll
-  for (int j = 0; j < PR; ++j) pp[j] = (uint32_t)(min(o0 + prow0 + (NT / 4) * j, OUT - 1) - o0);
+  for (int j = 0; j < PR; ++j) pp[j] = gidx::g_param_offset(o0, OUT, prow0, NT, j);
   // scale staging: threads 0..15 copy the step's 32 scales and 32 reciprocals
   const float* pst = s_tab + (size_t)ai * K;
   const float* pit = inv_tab + (size_t)ai * K;
@@ -231,8 +220,8 @@ k_grid(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
   // one K step: MFMAs on `cur` and Wq buffer `buf`, interleaved with producing
   // Wq(step+1) into the other buffer; then the raw store of `wst` into raw
   // buffer `buf` and a barrier.  The scheduler is asked for one MFMA, then two
-  // VALU instructions, repeated: with two wavefronts per SIMD the production
-  // work then runs under the MFMA pipeline instead of after it.
+  // VALU instructions, repeated, so the production work issues while the
+  // matrix pipe runs instead of after it.
   auto step_body = [&](const AF& cur, int buf, GP gprod, WR wst) {
     mfma_half(cur, buf, 0);
     produce(buf ^ 1, gprod);
@@ -418,15 +407,11 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_tiles = n_t_tiles * n_o_tiles;
-  const int b = blockIdx.x;
-  const int u = unit_base + (split == 1 ? b : (b & 7) + 8 * (b >> 4));
-  const int h = split == 1 ? 0 : (b >> 3) & 1;
-  const int jb = u >> 3;
-  const int ai = jb % n_grid;
-  const int T = (jb / n_grid) * 8 + (u & 7);
+  const gidx::Unit un =
+      gidx::unit_of_block(blockIdx.x, unit_base, split, n_grid, n_o_tiles, BM);
+  const int ai = un.ai, T = un.T, h = un.h;
   if (T >= n_tiles) return;
-  const int tt = T / n_o_tiles, ot = T - tt * n_o_tiles;
-  const int t0 = tt * BM * split + h * BM, o0 = ot * BN;
+  const int t0 = un.t0, o0 = un.o0;
   if (t0 >= N) {
     if (threadIdx.x == 0) partials[2 * ((size_t)ai * n_tiles + T) + h] = 0.0;
     return;
@@ -442,35 +427,25 @@ k_grid_pp(const _Float16* __restrict__ X, const _Float16* __restrict__ W,
 
   // whole-line loads: lane l covers row l/8 of the load's 8 rows and stores
   // its 16 bytes at position l%8, i.e. it reads piece (l%8) ^ (row & 7)
-  const int lrow = lane >> 3, lpos = lane & 7;
   const _Float16* xt = X + (size_t)t0 * K;
   uint32_t pa[ALD];  // byte offsets from xt of this lane's pieces (chunk 0)
 #pragma unroll
-  for (int i = 0; i < ALD; ++i) {
-    const int r = 8 * i + lrow;  // row within the wavefront's rows
-    const int row = min(t0 + wave * WMT + r, N - 1) - t0;
-    pa[i] = 2u * ((uint32_t)row * (uint32_t)K + 8 * (lpos ^ (r & 7)));
-  }
+  for (int i = 0; i < ALD; ++i) pa[i] = gidx::pp_act_offset(t0, N, K, wave, WMT, i, lane);
   const _Float16* wt = W + (size_t)o0 * K;
   uint32_t pw[2];  // this wavefront's two weight loads per chunk: group rows 16pc + 8i ..
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 64 * grp + 16 * pc + 8 * i + lrow;
-    const int go = min(o0 + r, OUT - 1) - o0;
-    pw[i] = 2u * ((uint32_t)go * (uint32_t)K + 8 * (lpos ^ (r & 7)));
-  }
+  for (int i = 0; i < 2; ++i) pw[i] = gidx::pp_w_offset(o0, OUT, K, grp, pc, i, lane);
   // per-group loads of the wavefront's group: wavefront 0 of the group the
   // parameters of its 64 rows, wavefront 1 the scales (lanes 0-31) and the
   // reciprocals (lanes 32-63, reached from the scale table's base: the
   // library places that table a short positive distance after the scales)
   const GroupParams* pgp = prm + (size_t)ai * ngroups * OUT;
-  const uint32_t pgo = 16u * (uint32_t)min(o0 + 64 * grp + lane, OUT - 1);
+  const uint32_t pgo = gidx::pp_param_offset(o0, OUT, grp, lane);
   const float* pgs = s_tab + (size_t)ai * K;
   // lanes 0 .. GC/4-1 the group's scales, the next GC/4 lanes its reciprocals
   // (further lanes repeat them: a load fills 64 x 16 bytes of LDS)
-  const int sl4 = lane % (GC / 2);
-  const uint32_t pso = 16 * (sl4 % (GC / 4)) +
-                       (sl4 < GC / 4 ? 0u : (uint32_t)((const char*)inv_tab - (const char*)s_tab));
+  const uint32_t pso =
+      gidx::pp_scale_offset(lane, GC, (uint32_t)((const char*)inv_tab - (const char*)s_tab));
 
   floatx4 acc[MBW][NBW];
 #pragma unroll
@@ -757,95 +732,82 @@ int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid) {
   return 128;
 }
 
-// The ping-pong kernel takes groups of 128 columns on the 8-wavefront tiles
-// when the reciprocal table lies a short positive distance after the scale
-// table (it reaches both through one base address); otherwise k_grid runs.
-template <int NW, int GS>
-static constexpr bool pp_shape() {
-  return NW == 8;
-}
-
+// The 8-wavefront tiles (512 and 256 tokens) run the ping-pong kernel, the
+// 4-wavefront 128-token tile runs k_grid.  The ping-pong kernel reaches the
+// reciprocal table from the scale table's base: search_plan places it right
+// after that table on the next 256-byte boundary, a positive distance of at
+// most 4 * 64 * 2^20 bytes (n_grid <= 64, in_features <= 2^20), which fits
+// the kernel's 32-bit lane offsets.
 template <int BM, int NW, int GS>
-static void launch_one(bool pp, unsigned blocks, int unit_base, int split, hipStream_t stream,
+static void launch_one(unsigned blocks, int unit_base, int split, hipStream_t stream,
                        const _Float16* X, const _Float16* W, const float* s_tab,
                        const float* inv_tab, const GroupParams* prm, double* partials, int N,
                        int K, int OUT, int nt, int no, int n_grid) {
-  if constexpr (pp_shape<NW, GS>()) {
-    if (pp) {
-      hipLaunchKernelGGL((k_grid_pp<BM, kGridBN, GS>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
-                         s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base,
-                         split);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((k_grid<BM, kGridBN, NW, GS>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
-                     s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base, split);
+  if constexpr (NW == 8)
+    hipLaunchKernelGGL((k_grid_pp<BM, kGridBN, GS>), dim3(blocks), dim3(NW * 64), 0, stream, X, W,
+                       s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base, split);
+  else
+    hipLaunchKernelGGL((k_grid<BM, kGridBN, NW, GS>), dim3(blocks), dim3(NW * 64), 0, stream, X,
+                       W, s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid, unit_base,
+                       split);
 }
 
 // Blocks of the whole-tile kernel that run at once on the current device
-// (compute units x resident blocks per unit), cached per device and kernel.
-template <int BM, int NW, int GS>
-static int64_t resident_blocks(bool pp) {
+// (compute units x resident blocks per unit), cached per device.
+template <int BM, int GS>
+static int64_t resident_blocks() {
   static std::mutex mu;
-  static std::map<int, int64_t> cache;  // key: 2 * device + pp
+  static std::map<int, int64_t> cache;  // key: device
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  pp = pp && pp_shape<NW, GS>();
-  const int key = 2 * dev + (pp ? 1 : 0);
   std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(key);
+  auto it = cache.find(dev);
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) {
-    if (pp)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid_pp<BM, kGridBN, GS>, NW * 64,
-                                                       0);
-    else
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid<BM, kGridBN, NW, GS>,
-                                                       NW * 64, 0);
-  }
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_grid_pp<BM, kGridBN, GS>, 512, 0);
   if (e != hipSuccess) return 0;
   const int64_t r = (int64_t)cus * per_cu;
-  cache[key] = r;
+  cache[dev] = r;
   return r;
 }
 
-template <int BM, int NW, int HBM, int HNW, int GS>
-static void launch_split(bool pp, int64_t units, hipStream_t stream, const _Float16* X,
+template <int BM, int HBM, int HNW, int GS>
+static void launch_split(int64_t units, hipStream_t stream, const _Float16* X,
                          const _Float16* W, const float* s_tab, const float* inv_tab,
                          const GroupParams* prm, double* partials, int N, int K, int OUT, int nt,
                          int no, int n_grid) {
-  const int64_t slots = resident_blocks<BM, NW, GS>(pp);
+  const int64_t slots = resident_blocks<BM, GS>();
   int64_t whole = units;
   if (slots > 0) {
     const int64_t rest = units % slots;
     if (units > slots && rest > 0 && rest % 8 == 0 && 2 * rest <= slots) whole = units - rest;
   }
-  launch_one<BM, NW, GS>(pp, (unsigned)whole, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials,
-                         N, K, OUT, nt, no, n_grid);
+  launch_one<BM, 8, GS>((unsigned)whole, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials, N, K,
+                        OUT, nt, no, n_grid);
   if (whole < units)  // whole and units are multiples of 8
-    launch_one<HBM, HNW, GS>(pp, (unsigned)(2 * (units - whole)), (int)whole, 2, stream, X, W,
-                             s_tab, inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
+    launch_one<HBM, HNW, GS>((unsigned)(2 * (units - whole)), (int)whole, 2, stream, X, W, s_tab,
+                             inv_tab, prm, partials, N, K, OUT, nt, no, n_grid);
 }
 
 template <int GS>
-static void launch_tiles(bool pp, int tile_m, int64_t units, hipStream_t stream,
-                         const _Float16* X, const _Float16* W, const float* s_tab,
-                         const float* inv_tab, const GroupParams* prm, double* partials, int N,
-                         int K, int OUT, int nt, int no, int n_grid) {
+static void launch_tiles(int tile_m, int64_t units, hipStream_t stream, const _Float16* X,
+                         const _Float16* W, const float* s_tab, const float* inv_tab,
+                         const GroupParams* prm, double* partials, int N, int K, int OUT, int nt,
+                         int no, int n_grid) {
   switch (tile_m) {
     case 512:
-      launch_split<512, 8, 256, 8, GS>(pp, units, stream, X, W, s_tab, inv_tab, prm, partials, N,
-                                       K, OUT, nt, no, n_grid);
+      launch_split<512, 256, 8, GS>(units, stream, X, W, s_tab, inv_tab, prm, partials, N, K, OUT,
+                                    nt, no, n_grid);
       break;
     case 256:
-      launch_split<256, 8, 128, 4, GS>(pp, units, stream, X, W, s_tab, inv_tab, prm, partials, N,
-                                       K, OUT, nt, no, n_grid);
+      launch_split<256, 128, 4, GS>(units, stream, X, W, s_tab, inv_tab, prm, partials, N, K, OUT,
+                                    nt, no, n_grid);
       break;
     default:
-      launch_one<128, 4, GS>(pp, (unsigned)units, 0, 1, stream, X, W, s_tab, inv_tab, prm,
-                             partials, N, K, OUT, nt, no, n_grid);
+      launch_one<128, 4, GS>((unsigned)units, 0, 1, stream, X, W, s_tab, inv_tab, prm, partials,
+                             N, K, OUT, nt, no, n_grid);
       break;
   }
 }
@@ -856,17 +818,15 @@ void launch_grid(int tile_m, int group, const void* X, const void* W, const floa
   const int64_t units = (nt * no + 7) / 8 * 8 * n_grid;
   const _Float16* Xh = (const _Float16*)X;
   const _Float16* Wh = (const _Float16*)W;
-  const uintptr_t ds = (uintptr_t)inv_tab - (uintptr_t)s_tab;
-  const bool pp = (uintptr_t)inv_tab > (uintptr_t)s_tab && ds < ((uintptr_t)1 << 31);
   if (group == 32)
-    launch_tiles<1>(pp, tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
-                    (int)K, (int)OUT, (int)nt, (int)no, n_grid);
+    launch_tiles<1>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
+                    (int)OUT, (int)nt, (int)no, n_grid);
   else if (group == 64)
-    launch_tiles<2>(pp, tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
-                    (int)K, (int)OUT, (int)nt, (int)no, n_grid);
+    launch_tiles<2>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
+                    (int)OUT, (int)nt, (int)no, n_grid);
   else
-    launch_tiles<4>(pp, tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N,
-                    (int)K, (int)OUT, (int)nt, (int)no, n_grid);
+    launch_tiles<4>(tile_m, units, stream, Xh, Wh, s_tab, inv_tab, prm, partials, (int)N, (int)K,
+                    (int)OUT, (int)nt, (int)no, n_grid);
 }
 
 }  // namespace awq
