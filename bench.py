@@ -42,7 +42,7 @@ sys.path.insert(0, ROOT)
 MFMA_F16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 fp16 flop/clk (dense)
 HBM_PEAK_GBS = 8000.0
 METRIC = "AWQ α-grid search TFLOP/s + MFMA util; quant/pack HBM GB/s (1 GPU)"
-DEFAULT_CONFIG = 2
+DEFAULT_CONFIG = 5   # the largest configuration: the 13B-style block, four searches
 
 
 def log(*a):
@@ -63,11 +63,11 @@ def pack_bytes(spec, group=128):
 
 
 def source_digest():
-    """Digest of the grid kernel's code (search_grid.hip and awq_device.h with
-    comments and blank lines removed and lines stripped), so that a counter
-    summary stays valid across edits of comments only."""
+    """Digest of the grid kernel's code (search_grid.hip, grid_index.h and
+    awq_device.h with comments and blank lines removed and lines stripped), so
+    that a counter summary stays valid across edits of comments only."""
     h = hashlib.sha256()
-    for f in ("search_grid.hip", "awq_device.h"):
+    for f in ("search_grid.hip", "grid_index.h", "awq_device.h"):
         src = open(os.path.join(ROOT, "post_bit_weight_awq_amd", "csrc", f)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         src = re.sub(r"//[^\n]*", "", src)
@@ -90,23 +90,26 @@ def grid_kernel_names(layers, cfg):
 
 
 def traffic_from_profiles(workload):
-    """HBM bytes per launch of the grid kernel from the committed PMC summary,
-    or None when there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", "search_grid_pmc_traffic.md")
-    if not os.path.exists(path):
-        return None
-    for line in open(path):
-        m = re.match(r"\s*traffic:\s*workload=(\S+)\s+source=(\S+)\s+bytes_per_launch=(\S+)", line)
-        if m and m.group(1) == workload and m.group(2) == source_digest():
-            return float(m.group(3))
+    """HBM bytes per launch of the grid kernel (the mean over the step's grid
+    launches) from the committed PMC summary, or None when there is none or the
+    kernel source changed since."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        for line in open(path):
+            m = re.match(r"\s*traffic:\s*workload=(\S+)\s+source=(\S+)\s+bytes_per_launch=(\S+)",
+                         line)
+            if m and m.group(1) == workload and m.group(2) == source_digest():
+                return float(m.group(3))
     return None
 
 
 def cpu_baseline(cfg_key, target_s):
-    """The oracle, as it stands, on the first layer: stats on all tokens, the
-    full 20-point search and pack on a leading cut of output rows sized for
-    about target_s seconds.  Reported in the metric's unit (TFLOP/s of search
-    flops over stats + search + pack time)."""
+    """The oracle, as it stands, on a bounded sample of the workload: for every
+    layer of the configuration, stats over all its tokens, then the full
+    20-point search and pack on a leading cut of its output rows, the cuts
+    sized so that the whole sample takes about target_s seconds.  Reported in
+    the metric's unit: search flops of the sampled rows over the sample's
+    stats + search + pack time."""
     import numpy as np
     import synth
     from oracle import awq_oracle as O
@@ -115,33 +118,43 @@ def cpu_baseline(cfg_key, target_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    spec, X, W = synth.make_layer(cfg_key, 0)
-    t0 = time.perf_counter()
-    sal = O.act_stats(X)
-    t_stats = time.perf_counter() - t0
-    # size the row cut from a probe of 1 grid point on 64 rows
-    rows = min(64, spec.out_features)
-    s, inv_s = O.scale_table(sal)
-    t0 = time.perf_counter()
-    O.tile_sq_error(X, W, s[5], inv_s[5], slice(0, spec.n_tokens), slice(0, rows))
-    per_row_alpha = (time.perf_counter() - t0) / rows
-    rows = int(max(8, min(spec.out_features, target_s / (20 * per_row_alpha + 1e-12))))
-    Wc = np.ascontiguousarray(W[:rows])
-    t0 = time.perf_counter()
-    res = O.search_layer(X, Wc, sal)
-    t_search = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    O.pack(Wc, res.s_best)
-    t_pack = time.perf_counter() - t0
-    flops = 2.0 * 20 * spec.n_tokens * spec.in_features * rows
+    layers = synth.CONFIGS[cfg_key].layers
+    per_layer_s = target_s / len(layers)
+    t_stats = t_search = t_pack = 0.0
+    flops = 0.0
+    parts = []
+    for li, spec in enumerate(layers):
+        _, X, W = synth.make_layer(cfg_key, li)
+        t0 = time.perf_counter()
+        sal = O.act_stats(X)
+        t_stats += time.perf_counter() - t0
+        # size the row cut from a probe of one grid point on 512 rows (smaller
+        # probes are dominated by per-call costs and undersize the cut)
+        rows = min(512, spec.out_features)
+        s, inv_s = O.scale_table(sal)
+        t0 = time.perf_counter()
+        O.tile_sq_error(X, W, s[5], inv_s[5], slice(0, spec.n_tokens), slice(0, rows))
+        per_row_alpha = (time.perf_counter() - t0) / rows
+        rows = int(max(8, min(spec.out_features, per_layer_s / (20 * per_row_alpha + 1e-12))))
+        Wc = np.ascontiguousarray(W[:rows])
+        del W
+        t0 = time.perf_counter()
+        res = O.search_layer(X, Wc, sal)
+        t_search += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.pack(Wc, res.s_best)
+        t_pack += time.perf_counter() - t0
+        flops += 2.0 * 20 * spec.n_tokens * spec.in_features * rows
+        parts.append(f"{spec.name} {spec.n_tokens}x{spec.in_features}: {rows} of "
+                     f"{spec.out_features} rows")
     return {
         "value": flops / (t_stats + t_search + t_pack) / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"layer {spec.name} of config {cfg_key}: stats over all {spec.n_tokens}x"
-                   f"{spec.in_features}, 20-point search and pack on the first {rows} of "
-                   f"{spec.out_features} output rows"),
+        "sample": (f"every layer of config {cfg_key} ({synth.CONFIGS[cfg_key].workload}): stats "
+                   f"over all tokens, 20-point search and pack on a leading cut of output rows ("
+                   + "; ".join(parts) + ")"),
         "seconds": {"stats": t_stats, "search": t_search, "pack": t_pack},
     }
 
@@ -194,12 +207,16 @@ def cold_measurements(awq, cfg, layers, calib):
         ms_stats = timed(lambda: awq.awq_act_stats(L["X"], out=L["sal"], workspace=L["sws"]))
         ms_pack = timed(lambda: awq.awq_pack(L["W"], L["s_best"], cfg, qweight=L["qw"],
                                              step=L["st"], zero=L["zr"]))
+        wb = L["W"].numel() * 2
         ms_read = timed(lambda: calib.awq_calib_read(L["X"].data_ptr(), xb, sink.data_ptr(),
                                                      4096, stream))
+        ms_read_w = timed(lambda: calib.awq_calib_read(L["W"].data_ptr(), wb, sink.data_ptr(),
+                                                       4096, stream))
         res[spec.name] = {"stats_gbs_cold": round(stats_bytes(spec) / (ms_stats * 1e-3) / 1e9, 1),
                           "pack_gbs_cold": round(pack_bytes(spec, cfg.group_size) /
                                                  (ms_pack * 1e-3) / 1e9, 1),
-                          "plain_read_of_X_gbs_cold": round(xb / (ms_read * 1e-3) / 1e9, 1)}
+                          "plain_read_of_X_gbs_cold": round(xb / (ms_read * 1e-3) / 1e9, 1),
+                          "plain_read_of_W_gbs_cold": round(wb / (ms_read_w * 1e-3) / 1e9, 1)}
     del flush
     out_buf = torch.empty(1024 * 512, dtype=torch.float32, device="cuda")
     n_iter = 1024
@@ -402,7 +419,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=DEFAULT_CONFIG, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0)
     ap.add_argument("--group", type=int, default=128, choices=[32, 64, 128],
                     help="quantization group size (ablation variants; the method uses 128)")
@@ -501,22 +518,20 @@ def main():
 
     names = ("stats", "prepare", "grid", "select", "pack")
 
-    def step(events=None):
-        """One pass of the hot path over every layer: saliency, search, pack.  With
-        events, the search runs stage by stage with an event between stages (the
-        per-stage breakdown); without, as one call, the way a caller runs it."""
+    def step(ev=None):
+        """One pass of the hot path over every layer: saliency, search (prepare,
+        grid, select), pack, with a HIP event before and after each stage on the
+        stream the calls launch on (torch's current stream)."""
         for li, L in enumerate(layers):
-            ev = events[li] if events is not None else None
+            e = ev[li] if ev is not None else None
 
             def mark(j):
-                if ev is not None:
-                    ev[j].record()
+                if e is not None:
+                    e[j].record()
             mark(0)
             awq.awq_act_stats(L["X"], out=L["sal"], workspace=L["sws"])
             mark(1)
-            stages = ((awq.STAGE_PREPARE, awq.STAGE_GRID, awq.STAGE_SELECT) if ev is not None
-                      else (awq.STAGE_ALL,))
-            for j, stg in enumerate(stages):
+            for j, stg in enumerate((awq.STAGE_PREPARE, awq.STAGE_GRID, awq.STAGE_SELECT)):
                 awq.awq_search_layer(L["X"], L["W"], L["sal"], cfg, workspace=L["ws"],
                                      losses=L["losses"], best_idx=L["best"],
                                      s_best=L["s_best"], stages=stg)
@@ -527,18 +542,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # per-stage breakdown (untimed pass): events on torch's current stream, which is
-    # the stream every call launches on; each event costs a few microseconds of queue
-    # time, so the headline below is timed on a separate pass without them
+    # the timed region: exactly args.steps steps, synchronized on both sides; the
+    # per-stage events inside it are the live kernel timings (each event adds a few
+    # microseconds of queue time, well under 1 % of a block step)
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in layers]
            for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    # the timed region: exactly args.steps steps, synchronized on both sides
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step()
+        step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
@@ -588,6 +599,24 @@ def main():
         measured = {"mfma_f16_loop_tflops": mfma_peak,
                     "note": "MFMA-only register loop with the grid kernel's instruction and "
                             "wavefront shape; *_cold: MALL cleared by a 512 MiB read first"}
+
+    def hbm_stage(stage, nbytes, plain_key):
+        """Bytes of the stage over all layers / the sum of its median launch
+        times, against the HBM peak and against a plain streaming read of the
+        same input (cold, same size) where one was measured."""
+        b = sum(nbytes(L["spec"]) for L in layers)
+        ms = sum(med(samples[stage][li]) for li in range(len(layers)))
+        gbs = b / (ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": b,
+             "per_layer": {L["spec"].name: kernels[L["spec"].name][stage + "_gbs"]
+                           for L in layers}}
+        if all(plain_key in kernels[L["spec"].name] for L in layers):
+            pr = {L["spec"].name: kernels[L["spec"].name][plain_key] for L in layers}
+            r["plain_read_gbs_cold"] = pr
+            r["frac_of_plain_read"] = {n: round(r["per_layer"][n] / pr[n], 3) for n in pr}
+        return r
+
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -613,7 +642,15 @@ def main():
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": traffic,
-                     "grid_ms_per_search": round(grid_ms / len(layers), 5)},
+                     "flops_per_search": {L["spec"].name: F[li] for li, L in enumerate(layers)},
+                     "grid_ms_per_search": {L["spec"].name: round(per["grid"][li], 5)
+                                            for li, L in enumerate(layers)},
+                     "frac_per_layer": {L["spec"].name: round(
+                         F[li] / (per["grid"][li] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+                         for li, L in enumerate(layers)},
+                     "stats": hbm_stage("stats", stats_bytes, "plain_read_of_X_gbs_cold"),
+                     "pack": hbm_stage("pack", lambda sp: pack_bytes(sp, cfg.group_size),
+                                       "plain_read_of_W_gbs_cold")},
         "kernels": kernels,
         "measured_peaks": measured,
     }

@@ -242,4 +242,4 @@ def test_committed_grid_profiles_match_the_grid_source():
             named += 1
             assert m.group(1) == digest, os.path.basename(p)
     assert named >= 3
-    assert bench.traffic_from_profiles("llama7b_q_proj_in4096_out4096_tok512") is not None
+    assert bench.traffic_from_profiles("llama13b_block_h5120_mlp13824_tok4096") is not None
