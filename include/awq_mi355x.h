@@ -31,7 +31,9 @@
  *     that is current on the calling thread.  The caller owns every buffer;
  *     the library never allocates or frees device memory and keeps no device
  *     state between calls.  Scratch memory is a caller-provided workspace whose
- *     size the matching *_workspace_size call returns.
+ *     size the matching *_workspace_size call returns; the one exception,
+ *     awq_act_stats_noalloc, uses a fixed array that is part of the library's
+ *     device code (one copy per GPU).
  *   - Device pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
  *     work and return; results are valid once the stream has reached them.
@@ -117,6 +119,22 @@ const char* awq_version(void);
 size_t awq_act_stats_workspace_size(int64_t n_tokens, int64_t in_features);
 int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal_out,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same statistics, bit for bit, without a workspace and without
+ * allocating anything: for callers that cannot allocate device memory (code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The caller still passes X and sal_out.  The partial
+ * sums go to a fixed 8 MiB scratch array that the library holds on each GPU
+ * it runs on until the process ends (its address is looked up on the first
+ * call on a device).  Shapes whose partials exceed it are rejected on the
+ * host with AWQ_ERR_WORKSPACE before anything is enqueued: shapes with
+ * n_tokens <= 8192 and n_tokens * in_features <= 2^22 need none, and the
+ * rest need (row chunks) x in_features x 8 bytes, e.g. 3.5 MiB for
+ * 4096 x 13824.  Every call on one GPU shares that GPU's array (each call
+ * writes all it reads, so nothing carries over), so calls that overlap on
+ * one GPU (different streams, or threads) race: serialize them. */
+int awq_act_stats_noalloc(const void* X, int64_t n_tokens, int64_t in_features, float* sal_out,
+                          void* stream);
 
 /* ------------------------------------------------------------------------
  * Steps 2-5: the alpha-grid search of one layer, all grid points in one pass.

@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import AwqConfig, AwqError, AwqSearchPlan, check, load  # noqa: F401
 from ._lib import STAGE_ALL, STAGE_GRID, STAGE_PREPARE, STAGE_SELECT  # noqa: F401
 
-__all__ = ["AwqConfig", "AwqError", "default_config", "awq_act_stats",
+__all__ = ["AwqConfig", "AwqError", "default_config", "awq_act_stats", "awq_act_stats_noalloc",
            "awq_act_stats_workspace_size", "awq_search_plan", "awq_search_workspace_size",
            "awq_search_layer", "awq_pack", "awq_w4a16_matmul", "awq_fold_inverse_scale", "awq_select_top_channels", "awq_weight_saliency",
            "SearchResult", "load"]
@@ -95,6 +95,23 @@ def awq_act_stats(X: torch.Tensor, *, out: Optional[torch.Tensor] = None,
         ctypes.c_void_p(_dev(out, "out", torch.float32, (k,))),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return out
+
+
+def awq_act_stats_noalloc(X: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                          stream=None) -> torch.Tensor:
+    """The same saliency through the entry point that allocates nothing (its
+    partials go to a fixed per-GPU scratch; overlapping calls on one GPU race).
+    Only ``out``, when not given, is allocated here."""
+    if X.dim() != 2:
+        raise ValueError("X must be [tokens, in_features]")
+    n, k = X.shape
+    with _on(stream):
+        if out is None:
+            out = torch.empty(k, dtype=torch.float32, device=X.device)
+    check(load().awq_act_stats_noalloc(
+        ctypes.c_void_p(_dev(X, "X", torch.float16, (n, k))), n, k,
+        ctypes.c_void_p(_dev(out, "out", torch.float32, (k,))), _stream(stream)))
     return out
 
 

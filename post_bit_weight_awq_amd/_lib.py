@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "AWQ_OK", -1: "AWQ_ERR_INVALID_ARG", -2: "AWQ_ERR_UNSUPPORTED
 #: every symbol the header declares
 EXPORTS = (
     "awq_default_config", "awq_last_error", "awq_version",
-    "awq_act_stats_workspace_size", "awq_act_stats",
+    "awq_act_stats_workspace_size", "awq_act_stats", "awq_act_stats_noalloc",
     "awq_search_plan_query", "awq_search_workspace_size", "awq_search_layer",
     "awq_search_layer_stages", "awq_pack", "awq_w4a16_matmul", "awq_fold_inverse_scale",
     "awq_select_top_channels",
@@ -71,6 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.awq_act_stats_workspace_size.restype = SZ
     lib.awq_act_stats.argtypes = [P, I64, I64, P, P, SZ, P]
     lib.awq_act_stats.restype = I32
+    lib.awq_act_stats_noalloc.argtypes = [P, I64, I64, P, P]
+    lib.awq_act_stats_noalloc.restype = I32
     lib.awq_search_plan_query.argtypes = [I64, I64, I64, ctypes.POINTER(AwqConfig),
                                           ctypes.POINTER(AwqSearchPlan)]
     lib.awq_search_plan_query.restype = I32

@@ -20,8 +20,18 @@
 // whole input is then in flight at once, and a second launch would cost more
 // than the parallelism it adds (measured 8.8 -> 6.4 us on 512 x 4096; on
 // 4096 x 5120 the two-pass form is faster, 15 vs 23 us).
+#include <map>
+#include <mutex>
+
 #include "awq_device.h"
 #include "awq_internal.h"
+
+// Scratch of the allocation-free entry point (awq_act_stats_noalloc): the
+// two-pass path's partial column sums, in a fixed array of which each GPU
+// holds its own copy until the process ends.  Host code never uses this name
+// as an address: it asks the runtime for the current device's copy once
+// (scratch_address) and passes that pointer to the kernels.
+static __device__ __align__(256) unsigned char scratch[awq::kStatsScratchBytes];
 
 namespace awq {
 
@@ -210,10 +220,39 @@ StatsPlan stats_plan(int64_t n_tokens, int64_t in_features) {
   return p;
 }
 
+static bool one_pass(int64_t n_tokens, int64_t in_features) {
+  return n_tokens <= 8192 && n_tokens * in_features <= kStats1MaxElems;
+}
+
+size_t stats_scratch_need(int64_t n_tokens, int64_t in_features) {
+  return one_pass(n_tokens, in_features) ? 0 : stats_plan(n_tokens, in_features).workspace_bytes;
+}
+
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
 hipError_t launch_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal,
                             void* workspace, hipStream_t stream) {
   const StatsPlan p = stats_plan(n_tokens, in_features);
-  if (n_tokens <= 8192 && n_tokens * in_features <= kStats1MaxElems) {
+  if (one_pass(n_tokens, in_features)) {
     hipLaunchKernelGGL(k_act_stats_1p, dim3((unsigned)((in_features + 63) / 64)),
                        dim3(kStats1Threads), 0, stream, (const uint4*)X, n_tokens, in_features,
                        sal);

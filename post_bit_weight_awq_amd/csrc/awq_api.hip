@@ -122,6 +122,25 @@ int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* s
                     "awq_act_stats launch");
 }
 
+int awq_act_stats_noalloc(const void* X, int64_t n_tokens, int64_t in_features, float* sal_out,
+                          void* stream) {
+  int rc;
+  if ((rc = check_dims(n_tokens, in_features, 1, true, false, 8))) return rc;
+  if ((rc = check_ptr(X, "X")) || (rc = check_ptr(sal_out, "sal_out"))) return rc;
+  const size_t need = awq::stats_scratch_need(n_tokens, in_features);
+  if (need > awq::kStatsScratchBytes)
+    return fail(AWQ_ERR_WORKSPACE,
+                "n_tokens=%lld x in_features=%lld needs %zu bytes of partial sums, above the "
+                "%zu-byte scratch of awq_act_stats_noalloc (awq_act_stats takes a workspace)",
+                (long long)n_tokens, (long long)in_features, need, awq::kStatsScratchBytes);
+  void* ws = nullptr;
+  if ((rc = hip_result(awq::scratch_address(&ws), "awq_act_stats_noalloc scratch address")))
+    return rc;
+  return hip_result(awq::launch_act_stats(X, n_tokens, in_features, sal_out, ws,
+                                          (hipStream_t)stream),
+                    "awq_act_stats_noalloc launch");
+}
+
 int awq_search_plan_query(int64_t n_tokens, int64_t in_features, int64_t out_features,
                           const awq_config* cfg, awq_search_plan* plan) {
   int rc;

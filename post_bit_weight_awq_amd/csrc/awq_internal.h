@@ -19,6 +19,12 @@ struct StatsPlan {
 StatsPlan stats_plan(int64_t n_tokens, int64_t in_features);
 hipError_t launch_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* sal,
                             void* workspace, hipStream_t stream);
+// Allocation-free statistics: bytes of partials a shape needs (0 when one
+// launch reads all of X), the fixed per-GPU scratch that holds them, and its
+// device address on the current GPU.
+constexpr size_t kStatsScratchBytes = (size_t)8 << 20;
+size_t stats_scratch_need(int64_t n_tokens, int64_t in_features);
+hipError_t scratch_address(void** out);
 
 // Quantizer settings: group of 32, 64 or 128 columns, 3- or 4-bit codes,
 // zero point (asymmetric) or symmetric.

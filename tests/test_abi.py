@@ -138,6 +138,20 @@ def test_stats_validation(lib):
     assert lib.awq_act_stats(FAKE, 10, 512, MISALIGNED, FAKE, need, None) == _lib.AWQ_ERR_INVALID_ARG
 
 
+def test_stats_noalloc_validation(lib):
+    # rejected on the host before the device is touched: bad pointers, bad
+    # shapes, and partial sums beyond the fixed scratch (2 row chunks x 2^20
+    # columns x 8 bytes = 16 MiB > 8 MiB)
+    f = lib.awq_act_stats_noalloc
+    assert f(None, 10, 512, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 10, 512, None, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 10, 512, MISALIGNED, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 0, 512, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 10, 12, FAKE, None) == _lib.AWQ_ERR_INVALID_ARG
+    assert f(FAKE, 8193, 1 << 20, FAKE, None) == _lib.AWQ_ERR_WORKSPACE
+    assert b"scratch" in lib.awq_last_error()
+
+
 def test_pack_validation(lib):
     cfg = _cfg(lib)
     assert lib.awq_pack(FAKE, FAKE, 100, 4, ctypes.byref(cfg), FAKE, FAKE, FAKE, None) \
