@@ -76,14 +76,19 @@ def source_digest():
 
 
 def grid_kernel_names(layers, cfg):
-    """Names of the grid-stage kernels the searches launch: the ping-pong
-    kernel on 512- and 256-token tiles, else k_grid."""
+    """Names of the grid-stage kernels the searches launch: the contraction of
+    the produced weight error on 256 x 256 tiles (layers of many token tiles),
+    else the fused kernels: ping-pong on 512- and 256-token tiles, k_grid on
+    128."""
     import post_bit_weight_awq_amd as P
     names = []
     for L in layers:
         sp = L["spec"]
         plan = P.awq_search_plan(sp.n_tokens, sp.in_features, sp.out_features, cfg)
-        nm = "k_grid_pp" if plan.tile_tokens in (512, 256) else "k_grid"
+        if plan.tile_out == 256:
+            nm = "k_grid_gemm"
+        else:
+            nm = "k_grid_pp" if plan.tile_tokens in (512, 256) else "k_grid"
         if nm not in names:
             names.append(nm)
     return " + ".join(names)
@@ -636,9 +641,9 @@ def main():
             for L in layers], "group_size": cfg.group_size, "w_bit": cfg.w_bit,
             "zero_point": bool(cfg.zero_point), "n_grid": cfg.n_grid},
         "roofline": {"bound": "mfma",
-                     "kernel": grid_kernel_names(layers, cfg) + " (fused alpha-grid search; "
-                               "per search: the whole-tile launch plus, when the last round "
-                               "is partly filled, the half-tile launch)",
+                     "kernel": grid_kernel_names(layers, cfg) + " (the grid stage of each "
+                               "search: all 20 grid points' contractions and squared errors; "
+                               "the weight-error production is in the prepare stage)",
                      "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": traffic,

@@ -12,8 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libawq_mi355x.so")
-SOURCES = ["act_stats.hip", "search.hip", "search_grid.hip", "pack.hip", "w4a16.hip",
-           "fold.hip", "select.hip", "awq_api.hip"]
+SOURCES = ["act_stats.hip", "search.hip", "search_grid.hip", "search_gemm.hip", "pack.hip",
+           "w4a16.hip", "fold.hip", "select.hip", "awq_api.hip"]
 # measured-peak references used by bench.py only (not part of the search library)
 CALIB_LIB = os.path.join(PKG, "libawq_calib.so")
 CALIB_SOURCES = ["calib.hip"]

@@ -34,13 +34,21 @@ struct QuantSpec {
   bool zero_point = true;
 };
 
+// Grid-stage kernels: the fused producer-and-contraction kernels (the weight
+// error rebuilt per token tile), or, for layers of many token tiles, the
+// weight error of every grid point produced once by the preparation stage and
+// a plain contraction (search_gemm.hip).
+enum GridKernel { kGridFused = 0, kGridGemm = 1 };
+constexpr int64_t kGemmMinTokenTiles = 4;  // 256-token tiles for the contraction path
+
 struct SearchPlan {
   int64_t tile_m, tile_n;        // tokens x outputs per tile
   int64_t n_t_tiles, n_o_tiles;  // tile counts
-  int kernel;                    // which tile kernel variant
+  int kernel;                    // GridKernel
   int64_t grid_blocks;           // blocks of the grid-kernel launch
   QuantSpec quant;
-  size_t off_partials, off_s, off_inv_s, off_params;
+  size_t off_partials, off_s, off_inv_s;
+  size_t off_params;             // fused: parameter records; contraction: weight error
   size_t bytes;
 };
 SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid,
@@ -51,6 +59,8 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
                          const SearchPlan& plan, int stage_mask, hipStream_t stream);
 
 int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid);
+void launch_grid_gemm(const void* X, const void* dW, double* partials, int64_t N, int64_t K,
+                      int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream);
 void launch_grid(int tile_m, int group, const void* X, const void* W, const float* s_tab,
                  const float* inv_tab, const GroupParams* prm, double* partials, int64_t N,
                  int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream);

@@ -1,6 +1,6 @@
-// Work-unit mapping and per-lane load offsets of the fused grid kernels
-// (search_grid.hip), written once for the device code and for a host-side
-// range check.  The kernels address their loads as a wavefront-uniform 64-bit
+// Work-unit mapping and per-lane load offsets of the grid kernels (the fused
+// kernels of search_grid.hip and the contraction of search_gemm.hip), written
+// once for the device code and for a host-side range check.  The kernels address their loads as a wavefront-uniform 64-bit
 // base plus a per-lane 32-bit offset; every offset below is computed in 32
 // bits, and the host check evaluates them at the largest shapes the library
 // accepts to show none of them wraps or leaves its buffer.
@@ -90,6 +90,36 @@ AWQ_HD uint32_t g_w_offset(int o0, int OUT, int K, int tid, int NT, int j) {
 // produced row prow0 + (NT / 4) j.
 AWQ_HD uint32_t g_param_offset(int o0, int OUT, int prow0, int NT, int j) {
   return (uint32_t)(imin(o0 + prow0 + (NT / 4) * j, OUT - 1) - o0);
+}
+
+// ---- k_grid_gemm (8 wavefronts; 256 x 256 tiles of the materialized weight
+// error, K steps of 64 columns, whole-line loads)
+// The j-th block an XCD receives (block b runs on XCD b % 8) takes token tile
+// j % nt of (grid point, output tile) pair 8 (j / nt) + xcd, pair index =
+// grid point * no + output tile: the token tiles of one pair run together on
+// one XCD and share its weight-error tile in that XCD's L2.
+struct GemmUnit {
+  int pair, ai, ot, tt, t0, o0;
+};
+AWQ_HD GemmUnit gemm_unit_of_block(int b, int nt, int no) {
+  GemmUnit r;
+  const int j = b >> 3;
+  r.pair = (j / nt) * 8 + (b & 7);
+  r.tt = j % nt;
+  r.ai = r.pair / no;
+  r.ot = r.pair - r.ai * no;
+  r.t0 = r.tt * 256;
+  r.o0 = r.ot * 256;
+  return r;
+}
+// Byte offset, from the first row of a 256-row tile, of the lane's 16-byte
+// piece of load i of wavefront w (8 rows x 128 bytes per load, row r of the
+// tile's rows clamped to the layer's last row, piece p stored at p ^ (r & 7)).
+AWQ_HD uint32_t gemm_offset(int row0, int rows, int K, int w, int loads_per_wave, int i,
+                            int lane) {
+  const int r = (w * loads_per_wave + i) * 8 + (lane >> 3);
+  const int row = imin(row0 + r, rows - 1) - row0;
+  return 2u * ((uint32_t)row * (uint32_t)K + 8 * ((lane & 7) ^ (r & 7)));
 }
 
 }  // namespace gidx

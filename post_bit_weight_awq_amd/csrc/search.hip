@@ -90,17 +90,35 @@ __device__ __forceinline__ float quad_max_step(float x) {
   const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
   return max3f(x, y, y);
 }
+// the value of lane CTRL & 3 of the lane's quad (CTRL a quad_perm [j, j, j, j])
+template <int CTRL>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 
-template <int G>
+// DW = false writes the parameter records (the fused grid kernel's input).
+// DW = true instead produces, for every grid point, the lane's part of the
+// fp16 weight error dW_i = fp16(Wq_i - W) of the layer into [grid point][OUT][K]
+// (the contraction kernel's input): codes rint(ws / step) clamped to
+// [-zero, qmax - zero], (q - zero) * step, times fp32(1/s) rounded once to
+// fp16, minus the fp16 weight rounded once.  The quotient is formed as
+// ws * (1/step), within 2.5 ulp of ws / step; where a per-group margin flags
+// it as that close to a half-integer, the code takes the IEEE division, so
+// every code equals the correctly rounded one (the fused kernel, which
+// rebuilds codes per token tile, keeps the product).  The parameters of four
+// grid points, finished by the four lanes of a team, reach every lane of the
+// team by DPP broadcasts.
+template <int G, bool DW>
 __global__ void __launch_bounds__(256)
 k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
-               GroupParams* __restrict__ prm, int OUT, int K, int n_grid, float qmax,
-               int symmetric) {
+               const float* __restrict__ inv_tab, GroupParams* __restrict__ prm,
+               _Float16* __restrict__ dw, int OUT, int K, int n_grid, float qmax, int symmetric) {
   constexpr int PL = G / 4;                      // weights per lane
   constexpr int CH4 = ParamsLds<G>::kChunk / 4;  // float4 per padded chunk
   constexpr int PG4 = ParamsLds<G>::kPerGrid / 4;
   constexpr int C4 = G / 4;                      // float4 of scales per group
-  extern __shared__ float4 s_lds4[];             // [n_grid][4 chunks][CH4 float4]
+  extern __shared__ float4 s_lds4[];             // [n_grid][4 chunks][CH4 float4] (x2 for DW)
+  float4* i_lds4 = s_lds4 + (size_t)n_grid * PG4;  // DW: the reciprocals, same layout
   const int ngroups = K / G;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
@@ -113,12 +131,14 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
   // scales of this group, every grid point: element e = (i, 16-byte column c4)
   for (int e = tid; e < n_grid * C4; e += 256) {
     const int i = e / C4, c4 = e - i * C4;
-    const float4 v = ((const float4*)(s_tab + (size_t)i * K + g * G))[c4];
-    s_lds4[i * PG4 + (c4 / (PL / 4)) * CH4 + c4 % (PL / 4)] = v;
+    const int dst = i * PG4 + (c4 / (PL / 4)) * CH4 + c4 % (PL / 4);
+    s_lds4[dst] = ((const float4*)(s_tab + (size_t)i * K + g * G))[c4];
+    if (DW) i_lds4[dst] = ((const float4*)(inv_tab + (size_t)i * K + g * G))[c4];
   }
   // the lane's weights, widened to fp32 once (exact) for the whole grid loop
   const uint4* wp = (const uint4*)(W + (size_t)o * K + k0);
   float wf[PL];
+  uint32_t wr[PL / 2];  // DW: the same weights as packed fp16 pairs
 #pragma unroll
   for (int v = 0; v < PL / 8; ++v) {
     const uint4 t = wp[v];
@@ -127,9 +147,11 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     for (int e = 0; e < 4; ++e) {
       wf[8 * v + 2 * e] = f16_lo(u[e]);
       wf[8 * v + 2 * e + 1] = f16_hi(u[e]);
+      wr[4 * v + e] = u[e];
     }
   }
   const float half = 0.5f * (qmax + 1.0f);  // 2^(b-1)
+  const float nz = opaque_neg_zero();
   __syncthreads();
   for (int i0 = 0; i0 < n_grid; i0 += 4) {
     float mnv[4], mxv[4];
@@ -174,23 +196,82 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     const float mn = l4 == 0 ? mnv[0] : l4 == 1 ? mnv[1] : l4 == 2 ? mnv[2] : mnv[3];
     const float mx = l4 == 0 ? mxv[0] : l4 == 1 ? mxv[1] : l4 == 2 ? mxv[2] : mxv[3];
     const int i = i0 + l4;
-    if (live && i < n_grid) {
-      float step, z;
-      if (symmetric) {
-        step = fmaxf(fabsf(mn), fabsf(mx)) / half;
-        if (step == 0.0f) step = 1.0f;
-        z = half;
-      } else {
-        step = (mx - mn) / qmax;
-        if (step == 0.0f) step = 1.0f;
-        z = rintf(-mn / step) + 0.0f;
+    float step, z;
+    if (symmetric) {
+      step = fmaxf(fabsf(mn), fabsf(mx)) / half;
+      if (step == 0.0f) step = 1.0f;
+      z = half;
+    } else {
+      step = (mx - mn) / qmax;
+      if (step == 0.0f) step = 1.0f;
+      z = rintf(-mn / step) + 0.0f;
+    }
+    GroupParams p;
+    p.step = step;
+    p.inv_step = 1.0f / step;
+    p.lo = -z;
+    p.hi = qmax - z;
+    if (!DW) {
+      if (live && i < n_grid) prm[((size_t)i * ngroups + g) * OUT + o] = p;
+      continue;
+    }
+    // products round monotonically, so every |ws / step| of the group is at
+    // most max(|min|, |max|) * (1/step): one margin (twice the 2^-21 |x|
+    // window, for its own roundings) flags the quotients near a tie
+    const float margin = 0.5f - fmaxf(fabsf(mn), fabsf(mx)) * p.inv_step * 0x1p-20f;
+    // every lane takes the four grid points' parameters from their lanes
+    GroupParams pj[4];
+    float mj[4];
+    pj[0] = {quad_bcast<0x00>(p.step), quad_bcast<0x00>(p.inv_step), quad_bcast<0x00>(p.lo),
+             quad_bcast<0x00>(p.hi)};
+    pj[1] = {quad_bcast<0x55>(p.step), quad_bcast<0x55>(p.inv_step), quad_bcast<0x55>(p.lo),
+             quad_bcast<0x55>(p.hi)};
+    pj[2] = {quad_bcast<0xAA>(p.step), quad_bcast<0xAA>(p.inv_step), quad_bcast<0xAA>(p.lo),
+             quad_bcast<0xAA>(p.hi)};
+    pj[3] = {quad_bcast<0xFF>(p.step), quad_bcast<0xFF>(p.inv_step), quad_bcast<0xFF>(p.lo),
+             quad_bcast<0xFF>(p.hi)};
+    mj[0] = quad_bcast<0x00>(margin);
+    mj[1] = quad_bcast<0x55>(margin);
+    mj[2] = quad_bcast<0xAA>(margin);
+    mj[3] = quad_bcast<0xFF>(margin);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ij = i0 + j;
+      if (ij >= n_grid) break;
+      const float4* sp = s_lds4 + ij * PG4 + l4 * CH4;
+      const float4* ip = i_lds4 + ij * PG4 + l4 * CH4;
+      uint32_t out[PL / 2];
+#pragma unroll
+      for (int v = 0; v < PL / 4; ++v) {
+        const float4 sv = sp[v], iv = ip[v];
+        const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
+        const float is[4] = {iv.x, iv.y, iv.z, iv.w};
+        float c[4];
+        bool redo = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = (wf[4 * v + e] * ss[e]) * pj[j].inv_step;
+          c[e] = rintf(x);
+          redo |= fabsf(x - c[e]) >= mj[j];
+        }
+        if (redo) {  // rare: the exact quotient where the margin flags it
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ws = wf[4 * v + e] * ss[e];
+            if (fabsf(ws * pj[j].inv_step - c[e]) >= mj[j]) c[e] = rintf(ws / pj[j].step);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] = med3(c[e], pj[j].lo, pj[j].hi) * pj[j].step;
+        out[2 * v] = sub_f16x2(mul_f32_to_f16x2(c[0], is[0], c[1], is[1], nz), wr[2 * v]);
+        out[2 * v + 1] = sub_f16x2(mul_f32_to_f16x2(c[2], is[2], c[3], is[3], nz), wr[2 * v + 1]);
       }
-      GroupParams p;
-      p.step = step;
-      p.inv_step = 1.0f / step;
-      p.lo = -z;
-      p.hi = qmax - z;
-      prm[((size_t)i * ngroups + g) * OUT + o] = p;
+      if (live) {
+        uint4* dst = (uint4*)(dw + ((size_t)ij * OUT + o) * K + k0);
+#pragma unroll
+        for (int v = 0; v < PL / 8; ++v)
+          dst[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
+      }
     }
   }
 }
@@ -253,13 +334,25 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_features, int n_grid,
                        const QuantSpec& qs) {
   SearchPlan p;
-  p.tile_m = grid_tile_m(n_tokens, out_features, n_grid);
   p.quant = qs;
-  p.tile_n = kGridBN;
-  p.kernel = 0;
-  p.n_t_tiles = (n_tokens + p.tile_m - 1) / p.tile_m;
-  p.n_o_tiles = (out_features + p.tile_n - 1) / p.tile_n;
-  p.grid_blocks = (p.n_t_tiles * p.n_o_tiles + 7) / 8 * 8 * n_grid;
+  // many token tiles: produce each grid point's weight error once and contract
+  // it (a fused kernel would rebuild it per token tile)
+  const bool gemm = (n_tokens + 255) / 256 >= kGemmMinTokenTiles;
+  if (gemm) {
+    p.kernel = kGridGemm;
+    p.tile_m = 256;
+    p.tile_n = 256;
+    p.n_t_tiles = (n_tokens + 255) / 256;
+    p.n_o_tiles = (out_features + 255) / 256;
+    p.grid_blocks = ((int64_t)n_grid * p.n_o_tiles + 7) / 8 * 8 * p.n_t_tiles;
+  } else {
+    p.kernel = kGridFused;
+    p.tile_m = grid_tile_m(n_tokens, out_features, n_grid);
+    p.tile_n = kGridBN;
+    p.n_t_tiles = (n_tokens + p.tile_m - 1) / p.tile_m;
+    p.n_o_tiles = (out_features + p.tile_n - 1) / p.tile_n;
+    p.grid_blocks = (p.n_t_tiles * p.n_o_tiles + 7) / 8 * 8 * n_grid;
+  }
   size_t off = 0;
   p.off_partials = off;
   off = align256(off + sizeof(double) * 2 * (size_t)n_grid * p.n_t_tiles * p.n_o_tiles);
@@ -268,7 +361,11 @@ SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_featur
   p.off_inv_s = off;
   off = align256(off + sizeof(float) * (size_t)n_grid * in_features);
   p.off_params = off;
-  off = align256(off + sizeof(GroupParams) * (size_t)n_grid * out_features * (in_features / qs.group));
+  if (gemm)  // fp16 weight error [grid point][out][in]
+    off = align256(off + sizeof(_Float16) * (size_t)n_grid * out_features * in_features);
+  else       // parameter records [grid point][group][out]
+    off = align256(off + sizeof(GroupParams) * (size_t)n_grid * out_features *
+                             (in_features / qs.group));
   p.bytes = off;
   return p;
 }
@@ -287,28 +384,49 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
   const float qmax = (float)((1 << p.quant.w_bit) - 1);
   const int sym = p.quant.zero_point ? 0 : 1;
 
+  const bool gemm = p.kernel == kGridGemm;
+  _Float16* dw = (_Float16*)(ws + p.off_params);
   if (stage_mask & 1) {  // prepare
     const int64_t nst = (int64_t)n_grid * K;
     hipLaunchKernelGGL(k_scale_table, dim3((unsigned)((nst + 255) / 256)), dim3(256), 0, stream,
                        sal, s_tab, inv_tab, K, n_grid, sal_floor);
     const dim3 pgrid((unsigned)((OUT + kParamsRows - 1) / kParamsRows), (unsigned)ng);
     const _Float16* Wh = (const _Float16*)W;
-    if (G == 32)
-      hipLaunchKernelGGL(k_group_params<32>, pgrid, dim3(256),
-                         sizeof(float) * ParamsLds<32>::kPerGrid * n_grid, stream, Wh, s_tab, prm,
-                         (int)OUT, (int)K, n_grid, qmax, sym);
-    else if (G == 64)
-      hipLaunchKernelGGL(k_group_params<64>, pgrid, dim3(256),
-                         sizeof(float) * ParamsLds<64>::kPerGrid * n_grid, stream, Wh, s_tab, prm,
-                         (int)OUT, (int)K, n_grid, qmax, sym);
-    else
-      hipLaunchKernelGGL(k_group_params<128>, pgrid, dim3(256),
-                         sizeof(float) * ParamsLds<128>::kPerGrid * n_grid, stream, Wh, s_tab,
-                         prm, (int)OUT, (int)K, n_grid, qmax, sym);
+    // LDS: the group's scales for every grid point (and, producing the weight
+    // error, their reciprocals)
+    const int tables = gemm ? 2 : 1;
+    if (G == 32) {
+      const size_t lds = sizeof(float) * ParamsLds<32>::kPerGrid * n_grid * tables;
+      if (gemm)
+        hipLaunchKernelGGL((k_group_params<32, true>), pgrid, dim3(256), lds, stream, Wh, s_tab,
+                           inv_tab, prm, dw, (int)OUT, (int)K, n_grid, qmax, sym);
+      else
+        hipLaunchKernelGGL((k_group_params<32, false>), pgrid, dim3(256), lds, stream, Wh, s_tab,
+                           inv_tab, prm, dw, (int)OUT, (int)K, n_grid, qmax, sym);
+    } else if (G == 64) {
+      const size_t lds = sizeof(float) * ParamsLds<64>::kPerGrid * n_grid * tables;
+      if (gemm)
+        hipLaunchKernelGGL((k_group_params<64, true>), pgrid, dim3(256), lds, stream, Wh, s_tab,
+                           inv_tab, prm, dw, (int)OUT, (int)K, n_grid, qmax, sym);
+      else
+        hipLaunchKernelGGL((k_group_params<64, false>), pgrid, dim3(256), lds, stream, Wh, s_tab,
+                           inv_tab, prm, dw, (int)OUT, (int)K, n_grid, qmax, sym);
+    } else {
+      const size_t lds = sizeof(float) * ParamsLds<128>::kPerGrid * n_grid * tables;
+      if (gemm)
+        hipLaunchKernelGGL((k_group_params<128, true>), pgrid, dim3(256), lds, stream, Wh, s_tab,
+                           inv_tab, prm, dw, (int)OUT, (int)K, n_grid, qmax, sym);
+      else
+        hipLaunchKernelGGL((k_group_params<128, false>), pgrid, dim3(256), lds, stream, Wh, s_tab,
+                           inv_tab, prm, dw, (int)OUT, (int)K, n_grid, qmax, sym);
+    }
   }
   if (stage_mask & 2) {  // grid
-    launch_grid((int)p.tile_m, G, X, W, s_tab, inv_tab, prm, partials, N, K, OUT, p.n_t_tiles,
-                p.n_o_tiles, n_grid, stream);
+    if (gemm)
+      launch_grid_gemm(X, dw, partials, N, K, OUT, p.n_t_tiles, p.n_o_tiles, n_grid, stream);
+    else
+      launch_grid((int)p.tile_m, G, X, W, s_tab, inv_tab, prm, partials, N, K, OUT, p.n_t_tiles,
+                  p.n_o_tiles, n_grid, stream);
   }
   if (stage_mask & 4) {  // select
     hipLaunchKernelGGL(k_argmin, dim3(1), dim3(kArgminThreads), 0, stream, partials,

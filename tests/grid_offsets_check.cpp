@@ -1,8 +1,9 @@
-// Host-side range check of the fused grid kernels' work-unit mapping and
-// 32-bit per-lane load offsets (post_bit_weight_awq_amd/csrc/grid_index.h,
-// the same functions the kernels call).  For shapes up to the largest the
-// library accepts (tokens <= 2^24, in/out features <= 2^20, in*out <= 2^34,
-// grid launches <= 2^23 blocks) it checks that
+// Host-side range check of the grid kernels' work-unit mapping and 32-bit
+// per-lane load offsets (post_bit_weight_awq_amd/csrc/grid_index.h, the same
+// functions the kernels call: the fused kernels and the contraction).  For
+// shapes up to the largest the library accepts (tokens <= 2^24, in/out
+// features <= 2^20, in*out <= 2^34, grid launches <= 2^23 blocks) it checks
+// that
 //   * every offset equals its exact 64-bit value (no 32-bit wrap) and every
 //     16-byte load it addresses lies inside its buffer, on the first and last
 //     token and output tiles of every kernel form;
@@ -158,6 +159,55 @@ static void check_units(int64_t N, int64_t OUT, int BM, int split, int n_grid, i
   }
 }
 
+// k_grid_gemm: offsets of the 256 x 256 tile starting at token t0 and output
+// o0 of grid point ai; the weight error is [n_grid][OUT][K] fp16
+static void check_gemm_tile(int t0, int o0, int64_t N, int64_t K, int64_t OUT) {
+  const int LOADS = 256 * 64 * 2 / 1024 / 8;
+  const int64_t nk = K / 64;
+  for (int w = 0; w < 8; ++w)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int i = 0; i < LOADS; ++i) {
+        const int r = (w * LOADS + i) * 8 + (lane >> 3);
+        const uint32_t oa = gemm_offset(t0, (int)N, (int)K, w, LOADS, i, lane);
+        int64_t row = t0 + r;
+        if (row > N - 1) row = N - 1;
+        const int64_t ea = 2 * ((row - t0) * K + 8 * ((lane & 7) ^ (r & 7)));
+        CHECK((int64_t)oa == ea, "gemm act N=%lld K=%lld t0=%d", (long long)N, (long long)K, t0);
+        CHECK(2 * t0 * K + ea + (nk - 1) * 128 + 16 <= 2 * N * K, "gemm act end");
+        const uint32_t ob = gemm_offset(o0, (int)OUT, (int)K, w, LOADS, i, lane);
+        int64_t orow = o0 + r;
+        if (orow > OUT - 1) orow = OUT - 1;
+        const int64_t eb = 2 * ((orow - o0) * K + 8 * ((lane & 7) ^ (r & 7)));
+        CHECK((int64_t)ob == eb, "gemm dw OUT=%lld K=%lld o0=%d", (long long)OUT, (long long)K, o0);
+        CHECK(2 * o0 * K + eb + (nk - 1) * 128 + 16 <= 2 * OUT * K, "gemm dw end");
+        CHECK(r < 256, "gemm tile row");
+      }
+}
+
+// every (pair, token tile) of the contraction launch is taken by exactly one
+// block that passes the early return, with its tile inside the layer
+static void check_gemm_units(int64_t N, int64_t OUT, int n_grid, bool all) {
+  const int64_t nt = cdiv(N, 256), no = cdiv(OUT, 128 * 2), pairs = n_grid * no;
+  const int64_t blocks = cdiv(pairs, 8) * 8 * nt;
+  std::vector<uint8_t> seen;
+  if (all) seen.assign((size_t)(pairs * nt), 0);
+  for (int64_t b = 0; b < blocks; ++b) {
+    if (!all && b >= 4096 && b < blocks - 4096) b = blocks - 4096;
+    const GemmUnit un = gemm_unit_of_block((int)b, (int)nt, (int)no);
+    if (un.pair >= pairs) continue;
+    CHECK(un.ai >= 0 && un.ai < n_grid && un.ot >= 0 && un.ot < no && un.tt >= 0 && un.tt < nt,
+          "gemm unit %lld", (long long)b);
+    CHECK(un.t0 < N && un.o0 < OUT, "gemm tile origin");
+    if (all) {
+      const size_t slot = (size_t)(un.pair * nt + un.tt);
+      CHECK(!seen[slot], "gemm unit twice");
+      seen[slot] = 1;
+    }
+  }
+  if (all)
+    for (size_t i = 0; i < seen.size(); ++i) CHECK(seen[i], "gemm unit %zu missed", i);
+}
+
 int main() {
   const int64_t MAXT = (int64_t)1 << 24, MAXF = (int64_t)1 << 20, MAXW = (int64_t)1 << 34;
   const int64_t MAXBLOCKS = (int64_t)1 << 23;
@@ -212,6 +262,20 @@ int main() {
               check_units(N, OUT, BM / 2, 2, n_grid, whole, units, all);
             }
           }
+      }
+  // the contraction path (layers of at least four 256-token tiles)
+  for (int64_t N : Ns)
+    for (int64_t K : Ks)
+      for (int64_t OUT : OUTs) {
+        if (OUT * K > MAXW || N < 769) continue;
+        for (int n_grid : grids) {
+          const int64_t nt = cdiv(N, 256), no = cdiv(OUT, 256);
+          if (cdiv(n_grid * no, 8) * 8 * nt > MAXBLOCKS) continue;
+          ++shapes;
+          for (int64_t tt : {(int64_t)0, nt - 1})
+            for (int64_t ot : {(int64_t)0, no - 1}) check_gemm_tile((int)(tt * 256), (int)(ot * 256), N, K, OUT);
+          check_gemm_units(N, OUT, n_grid, n_grid * no * nt <= ((int64_t)1 << 20));
+        }
       }
   if (fails) {
     printf("%d violations over %d shapes\n", fails, shapes);

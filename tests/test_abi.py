@@ -109,12 +109,18 @@ def test_search_workspace_too_small(lib):
     assert rc == _lib.AWQ_ERR_WORKSPACE
 
 
-def test_search_plan_layout(lib):
+@pytest.mark.parametrize("n", [500, 1000])
+def test_search_plan_layout(lib, n):
+    # n = 500: two 256-token tiles, the fused grid kernel and its parameter
+    # table; n = 1000: four tiles, the contraction path and its weight error
     cfg = _cfg(lib)
     plan = _lib.AwqSearchPlan()
-    assert lib.awq_search_plan_query(1000, 4096, 1000, ctypes.byref(cfg), ctypes.byref(plan)) == 0
-    assert plan.n_token_tiles == -(-1000 // plan.tile_tokens)
+    assert lib.awq_search_plan_query(n, 4096, 1000, ctypes.byref(cfg), ctypes.byref(plan)) == 0
+    assert plan.n_token_tiles == -(-n // plan.tile_tokens)
     assert plan.n_out_tiles == -(-1000 // plan.tile_out)
+    contraction = n >= 769
+    assert (plan.tile_tokens, plan.tile_out) == ((256, 256) if contraction else
+                                                 (plan.tile_tokens, 128))
     regions = sorted([
         (plan.partials_offset, 16 * 20 * plan.n_token_tiles * plan.n_out_tiles),
         (plan.scales_offset, 4 * 20 * 4096)])
@@ -123,9 +129,11 @@ def test_search_plan_layout(lib):
     assert regions[-1][0] + regions[-1][1] <= plan.workspace_bytes
     for off in (plan.partials_offset, plan.scales_offset):
         assert off % 256 == 0
-    # scale tables and per-group parameters dominate; there is no N x OUT buffer
-    params = 16 * 20 * 1000 * (4096 // 128)
-    assert plan.workspace_bytes < params + 2 * 4 * 20 * 4096 + 16 * 20 * 64 + 4096
+    # the scale tables and either the per-group parameters or the fp16 weight
+    # error of every grid point dominate; there is no N x OUT buffer
+    payload = 2 * 20 * 1000 * 4096 if contraction else 16 * 20 * 1000 * (4096 // 128)
+    assert payload < plan.workspace_bytes
+    assert plan.workspace_bytes < payload + 2 * 4 * 20 * 4096 + 16 * 20 * 64 + 4096
 
 
 def test_stats_validation(lib):

@@ -255,7 +255,7 @@ def test_search_edge_shapes(awq, n, k, o, n_grid):
 
 
 @pytest.mark.parametrize("n,k,o", [(700, 256, 2048), (300, 256, 2048), (700, 256, 2000),
-                                   (700, 1024, 2048), (1000, 384, 1970)])
+                                   (700, 1024, 2048), (760, 384, 1970)])
 def test_search_split_last_round(awq, n, k, o):
     """Shapes whose work units fill the chip 2.5 times: the last half round runs
     as half-height tiles, with ragged token tiles (the second half of the last
@@ -264,6 +264,7 @@ def test_search_split_last_round(awq, n, k, o):
     _say(f"search split last round {n}x{k}->{o}")
     _, X, W = synth.make_custom(n, k, o, seed=n + o)
     Xd, Wd, sal, res = run_layer(awq, X, W)
+    assert res.plan.tile_out == 128  # the fused kernels (fewer than four 256-token tiles)
     ref = O.search_layer(X, W, host(sal))
     losses = host(res.losses)
     rel = np.abs(losses - ref.losses) / ref.losses
@@ -390,6 +391,134 @@ def test_explicit_stream_argument(awq):
     best = int(host(res.best_idx)[0])
     check_best(best, ref.losses)
     check_pack(host(qw), host(st), host(zr), O.pack(W, ref.s[best]), "explicit stream")
+
+
+# ------------------------- layers of many token tiles: the contraction path
+# At least four 256-token tiles: the preparation stage writes every grid
+# point's weight error dW_i = fp16(Wq_i - W) once and the grid stage contracts
+# it (tiles of 256 tokens x 256 outputs).
+GEMM_CASES = [
+    ("ragged", dict(n=1000, k=384, o=300)),     # last token tile 232 rows, last output tile 44
+    ("exact", dict(n=1024, k=256, o=512)),
+    ("wide_k", dict(n=800, k=11008, o=257)),    # 86 column groups of 128; ragged outputs
+]
+
+
+@pytest.mark.parametrize("name,shape", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_search_contraction_path_matches_oracle(awq, name, shape):
+    n, k, o = shape["n"], shape["k"], shape["o"]
+    _say(f"contraction path {name}: {n}x{k}->{o}")
+    _, X, W = synth.make_custom(n, k, o, seed=n + k + o, token_scale=True)
+    Xd, Wd, sal, res = run_layer(awq, X, W)
+    assert (res.plan.tile_tokens, res.plan.tile_out) == (256, 256)
+    sal_h = host(sal)
+    ref = O.search_layer(X, W, sal_h)
+    losses = host(res.losses)
+    rel = np.abs(losses - ref.losses) / ref.losses
+    best = int(host(res.best_idx)[0])
+    _say(f"  max rel loss diff {rel.max():.3e}; best gpu {best} oracle {ref.best}")
+    assert np.all(rel <= LOSS_RTOL)
+    check_best(best, ref.losses)
+    assert np.array_equal(host(res.s_best).view(np.uint32), ref.s[best].view(np.uint32))
+
+
+@pytest.mark.parametrize("group,w_bit,zp", [(64, 4, True), (32, 4, True), (128, 3, True),
+                                            (128, 4, False), (32, 3, False)])
+def test_search_contraction_path_quantizer_variants(awq, group, w_bit, zp):
+    n, k, o = 1061, 512, 260
+    _say(f"contraction path variant g{group} b{w_bit} zp{zp}")
+    _, X, W = synth.make_custom(n, k, o, seed=group + w_bit, token_scale=True)
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    cfg = awq.default_config(group_size=group, w_bit=w_bit, zero_point=zp)
+    res = awq.awq_search_layer(Xd, Wd, sal, cfg)
+    torch.cuda.synchronize()
+    assert res.plan.tile_tokens == 256
+    ref = O.search_layer(X, W, host(sal), group=group, w_bit=w_bit, zero_point=zp)
+    losses = host(res.losses)
+    assert np.all(np.abs(losses - ref.losses) <= LOSS_RTOL * ref.losses)
+    check_best(int(host(res.best_idx)[0]), ref.losses)
+
+
+@pytest.mark.parametrize("group,w_bit,zp", [(128, 4, True), (32, 3, False)])
+def test_contraction_weight_error_matches_oracle(awq, group, w_bit, zp):
+    """The weight error the preparation stage writes for every grid point,
+    dW_i = fp16(Wq_i - W), bit for bit against the oracle's fake-quantized
+    weight minus W (the fp16 difference of two fp16 values, one rounding).
+    The kernel takes the exact quotient wherever its reciprocal product lies
+    near a tie, so its codes are the oracle's; the rule for codes decided at
+    a .5 tie would still admit differences only there (at most 1e-6 of the
+    elements, each one code), and none occurs."""
+    n, k, o = 1024, 384, 300
+    _say(f"contraction weight error {n}x{k}->{o} g{group} b{w_bit} zp{zp}")
+    _, X, W = synth.make_custom(n, k, o, seed=5, token_scale=True)
+    Xd, Wd = dev(X), dev(W)
+    sal = awq.awq_act_stats(Xd)
+    cfg = awq.default_config(group_size=group, w_bit=w_bit, zero_point=zp)
+    res = awq.awq_search_layer(Xd, Wd, sal, cfg, stages=awq._lib.STAGE_PREPARE)
+    torch.cuda.synchronize()
+    n_grid = 20
+    a256 = lambda v: (v + 255) // 256 * 256
+    off_inv = a256(res.plan.scales_offset + 4 * n_grid * k)
+    off_dw = a256(off_inv + 4 * n_grid * k)
+    dw = host(res.workspace[off_dw:off_dw + 2 * n_grid * o * k].view(torch.float16))
+    dw = dw.reshape(n_grid, o, k)
+    s_tab, inv_s = O.scale_table(host(sal))
+    diff = ties = 0
+    for i in range(n_grid):
+        gq = O.quantize(O.scaled_weights(W, s_tab[i]), group, w_bit, zp)
+        wq = O.dequantize(gq, inv_s[i], group)
+        want = (wq.astype(np.float64) - W.astype(np.float64)).astype(np.float16)
+        bad = want.view(np.uint16) != dw[i].view(np.uint16)
+        assert not (bad & ~gq.tie).any(), i  # a difference only at a near-tie code
+        diff += int(bad.sum())
+        ties += int(gq.tie.sum())
+    _say(f"  {diff} of {n_grid * o * k} weight-error elements differ ({ties} near a tie)")
+    assert diff <= 1e-6 * n_grid * o * k
+    assert diff == 0, "the producer takes the exact quotient near ties"
+
+
+def test_contraction_grid_stage_repeated(awq):
+    """Grid and select stages rerun on one prepared workspace give bitwise the
+    same losses (fixed per-tile partial slots, fixed-order sums)."""
+    n, k, o = 1100, 512, 600
+    _, X, W = synth.make_custom(n, k, o, seed=9)
+    Xd, Wd, sal, res = run_layer(awq, X, W)
+    assert res.plan.tile_tokens == 256
+    first = host(res.losses).copy()
+    for _ in range(3):
+        again = awq.awq_search_layer(Xd, Wd, sal, workspace=res.workspace,
+                                     stages=awq._lib.STAGE_GRID | awq._lib.STAGE_SELECT)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(again.losses).view(np.uint64), first.view(np.uint64))
+
+
+def test_contraction_path_replays_in_a_hip_graph(awq):
+    """Statistics, the contraction-path search and pack captured in one HIP
+    graph and replayed with eager work between replays: every replay equals
+    the eager run bit for bit."""
+    _, X, W = synth.make_custom(1024, 512, 512, seed=13)
+    Xd, Wd = dev(X), dev(W)
+
+    def run():
+        sal = awq.awq_act_stats(Xd)
+        res = awq.awq_search_layer(Xd, Wd, sal)
+        q, st, z = awq.awq_pack(Wd, res.s_best)
+        return sal, res.losses, res.best_idx, res.s_best, q, st, z
+
+    ref = [t.clone() for t in run()]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    for rep in range(3):
+        junk = torch.randn(1 << 20, device="cuda")
+        junk.mul_(2.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {rep}"
 
 
 # ----------------------------------- full-size layers against the oracle
@@ -606,7 +735,7 @@ def test_variant_search_and_pack_match_oracle(awq, group, w_bit, zp):
 
 @pytest.mark.parametrize("n,k,o,group,w_bit,zp", [(700, 1024, 2048, 64, 4, True),
                                                   (700, 1024, 2000, 32, 4, True),
-                                                  (1000, 640, 1970, 32, 3, False)])
+                                                  (760, 640, 1970, 32, 3, False)])
 def test_variant_split_last_round(awq, n, k, o, group, w_bit, zp):
     """Groups of 64 and 32 columns on the 512-token tile with the partial last
     round on the 256-token tile (ragged token tiles and last output tiles): all

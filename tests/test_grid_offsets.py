@@ -46,3 +46,7 @@ def test_grid_kernels_use_the_checked_index_helpers():
         assert re.search(r"gidx::%s\(" % fn, src), fn
     # no second copy of the mapping in the kernels
     assert "jb % n_grid" not in src
+    gemm = open(os.path.join(CSRC, "search_gemm.hip")).read()
+    assert '#include "grid_index.h"' in gemm
+    for fn in ("gemm_unit_of_block", "gemm_offset"):
+        assert re.search(r"gidx::%s\(" % fn, gemm), fn
