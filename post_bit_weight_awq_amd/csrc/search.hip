@@ -58,13 +58,14 @@ k_scale_table(const float* __restrict__ sal, float* __restrict__ s_tab,
 // finishes grid point i0 + j, so the three divisions run on all lanes at once.
 // Records are written in the layout [grid point][group][row].
 constexpr int kParamsRows = 64;
-// LDS copy of one grid point's G scales: four G/4-float chunks (one per team
-// lane), each padded by 4 floats so the four chunks a wavefront reads at once
-// sit in different banks.
+// LDS copy of the group's G scales (and reciprocals) for every grid point,
+// [grid point][G] floats.  Lane j of a team owns the 8-column pieces j, j + 4,
+// j + 8, ... of the group, so the four lanes of a team read (and the
+// producer writes) 64 contiguous bytes per instruction, and their scale
+// reads cover 128 contiguous bytes of a row (every bank once).
 template <int G>
 struct ParamsLds {
-  static constexpr int kChunk = G / 4 + 4;
-  static constexpr int kPerGrid = 4 * kChunk;
+  static constexpr int kPerGrid = G;
 };
 
 __device__ __forceinline__ float min3f(float a, float b, float c) {
@@ -113,12 +114,11 @@ __global__ void __launch_bounds__(256)
 k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
                const float* __restrict__ inv_tab, GroupParams* __restrict__ prm,
                _Float16* __restrict__ dw, int OUT, int K, int n_grid, float qmax, int symmetric) {
-  constexpr int PL = G / 4;                      // weights per lane
-  constexpr int CH4 = ParamsLds<G>::kChunk / 4;  // float4 per padded chunk
-  constexpr int PG4 = ParamsLds<G>::kPerGrid / 4;
-  constexpr int C4 = G / 4;                      // float4 of scales per group
-  extern __shared__ float4 s_lds4[];             // [n_grid][4 chunks][CH4 float4] (x2 for DW)
-  float4* i_lds4 = s_lds4 + (size_t)n_grid * PG4;  // DW: the reciprocals, same layout
+  constexpr int PL = G / 4;   // weights per lane
+  constexpr int NP = PL / 8;  // 8-column pieces per lane: j, j + 4, ... of the group
+  constexpr int C4 = G / 4;   // float4 of scales per group and grid point
+  extern __shared__ float4 s_lds4[];               // [n_grid][G / 4] float4 (x2 for DW)
+  float4* i_lds4 = s_lds4 + (size_t)n_grid * C4;   // DW: the reciprocals, same layout
   const int ngroups = K / G;
   const int g = blockIdx.y;
   const int tid = threadIdx.x;
@@ -126,22 +126,21 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
   const int o_raw = blockIdx.x * kParamsRows + (tid >> 2);
   const bool live = o_raw < OUT;
   const int o = live ? o_raw : OUT - 1;
-  const int k0 = g * G + l4 * PL;
 
   // scales of this group, every grid point: element e = (i, 16-byte column c4)
   for (int e = tid; e < n_grid * C4; e += 256) {
     const int i = e / C4, c4 = e - i * C4;
-    const int dst = i * PG4 + (c4 / (PL / 4)) * CH4 + c4 % (PL / 4);
-    s_lds4[dst] = ((const float4*)(s_tab + (size_t)i * K + g * G))[c4];
-    if (DW) i_lds4[dst] = ((const float4*)(inv_tab + (size_t)i * K + g * G))[c4];
+    s_lds4[e] = ((const float4*)(s_tab + (size_t)i * K + g * G))[c4];
+    if (DW) i_lds4[e] = ((const float4*)(inv_tab + (size_t)i * K + g * G))[c4];
   }
-  // the lane's weights, widened to fp32 once (exact) for the whole grid loop
-  const uint4* wp = (const uint4*)(W + (size_t)o * K + k0);
+  // the lane's weights (pieces l4 + 4 v), widened to fp32 once (exact) for the
+  // whole grid loop
+  const uint4* wp = (const uint4*)(W + (size_t)o * K + (size_t)g * G);
   float wf[PL];
   uint32_t wr[PL / 2];  // DW: the same weights as packed fp16 pairs
 #pragma unroll
-  for (int v = 0; v < PL / 8; ++v) {
-    const uint4 t = wp[v];
+  for (int v = 0; v < NP; ++v) {
+    const uint4 t = wp[4 * v + l4];
     const uint32_t u[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -158,14 +157,15 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = min(i0 + j, n_grid - 1);
-      const float4* sp = s_lds4 + i * PG4 + l4 * CH4;
+      // the scales of piece l4 + 4 (v / 2), half v % 2
+      const float4* sp = s_lds4 + i * C4 + 2 * l4;
       // ws = fp32(w * s): the product of the exact fp32 widening, rounded once.
       // The compiler knows products are canonical, so fminf / fmaxf chains
       // become v_min3 / v_max3 with no canonicalizing instructions.
       float mn, mx;
 #pragma unroll
       for (int v = 0; v < PL / 4; ++v) {
-        const float4 sv = sp[v];
+        const float4 sv = sp[8 * (v >> 1) + (v & 1)];
         const float a = wf[4 * v] * sv.x;
         const float b = wf[4 * v + 1] * sv.y;
         const float c = wf[4 * v + 2] * sv.z;
@@ -238,12 +238,12 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
     for (int j = 0; j < 4; ++j) {
       const int ij = i0 + j;
       if (ij >= n_grid) break;
-      const float4* sp = s_lds4 + ij * PG4 + l4 * CH4;
-      const float4* ip = i_lds4 + ij * PG4 + l4 * CH4;
+      const float4* sp = s_lds4 + ij * C4 + 2 * l4;
+      const float4* ip = i_lds4 + ij * C4 + 2 * l4;
       uint32_t out[PL / 2];
 #pragma unroll
       for (int v = 0; v < PL / 4; ++v) {
-        const float4 sv = sp[v], iv = ip[v];
+        const float4 sv = sp[8 * (v >> 1) + (v & 1)], iv = ip[8 * (v >> 1) + (v & 1)];
         const float ss[4] = {sv.x, sv.y, sv.z, sv.w};
         const float is[4] = {iv.x, iv.y, iv.z, iv.w};
         float c[4];
@@ -267,10 +267,10 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
         out[2 * v + 1] = sub_f16x2(mul_f32_to_f16x2(c[2], is[2], c[3], is[3], nz), wr[2 * v + 1]);
       }
       if (live) {
-        uint4* dst = (uint4*)(dw + ((size_t)ij * OUT + o) * K + k0);
+        uint4* dst = (uint4*)(dw + ((size_t)ij * OUT + o) * K + (size_t)g * G);
 #pragma unroll
-        for (int v = 0; v < PL / 8; ++v)
-          dst[v] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
+        for (int v = 0; v < NP; ++v)
+          dst[4 * v + l4] = make_uint4(out[4 * v], out[4 * v + 1], out[4 * v + 2], out[4 * v + 3]);
       }
     }
   }
