@@ -2,24 +2,27 @@
 """Benchmark of the AWQ per-layer search path on one MI355X.
 
 A step is one pass of the whole path over every searched layer of the
-workload: saliency (awq_act_stats), the alpha-grid search (awq_search_layer:
-prepare, fused grid kernel, select) and packing at the chosen alpha
-(awq_pack).  Inputs are seeded synthetic tensors (synth/), resident in HBM
-before timing starts.  The line printed on stdout:
+workload, stage after stage on one stream: saliency (awq_act_stats), the
+alpha-grid search (awq_search_layer in its three stages: prepare, grid,
+select) and packing at the chosen alpha (awq_pack).  Inputs are seeded
+synthetic tensors (synth/), resident in HBM before timing starts.  The line
+printed on stdout:
 
   value        search flops of the step (20 grid points x 2 N in out, summed
                over layers) / step time, TFLOP/s; the step time is the wall
-               clock of --steps steps run back to back (each search one call),
-               synchronized on both sides, after --warmup steps and an untimed
-               pass that records the per-stage events
-  roofline     the dominant kernel (the fused grid kernel): algorithmic flops
-               per search / the mean time of the search's grid launches, from
-               HIP events recorded on the launch stream, against the fp16 dense
-               MFMA peak; traffic is HBM bytes per search from the committed
-               rocprofv3 counter summary
-  kernels      per-kernel times, TFLOP/s and GB/s (stats and pack against HBM),
-               and the same two calls timed cold (last-level cache cleared
-               first) beside a plain streaming read of X
+               clock of --steps steps run back to back, synchronized on both
+               sides, after --warmup steps
+  roofline     the dominant kernel (the grid stage: the contraction of the
+               produced weight error on layers of many token tiles, else the
+               fused kernels): algorithmic flops per search / the time of the
+               search's grid stage, from HIP events recorded around each stage
+               on its launch stream inside the timed steps, against the fp16
+               dense MFMA peak; traffic is HBM bytes per launch from the
+               committed rocprofv3 counter summary; stats and pack against the
+               HBM peak and a cold plain read of the same input
+  kernels      per-stage times, TFLOP/s and GB/s, and stats and pack timed cold
+               (last-level cache cleared first) beside a plain streaming read
+               of X and of W
   measured_peaks  an MFMA-only loop (libawq_calib.so), for comparison with the
                published peak
   cpu_baseline the CPU oracle on a bounded sample of the same workload
@@ -62,17 +65,34 @@ def pack_bytes(spec, group=128):
     return 2.0 * w + 0.5 * w + 4.0 * w / group + 4.0 * spec.in_features
 
 
+def weight_error_bytes(spec, n_grid=20):
+    """HBM bytes of the contraction path's preparation stage: W read once, the
+    fp16 weight error of every grid point written (the scale table and the
+    saliency are a few KB)."""
+    w = spec.out_features * spec.in_features
+    return 2.0 * w + 2.0 * n_grid * w
+
+
 def source_digest():
-    """Digest of the grid kernel's code (search_grid.hip, grid_index.h and
-    awq_device.h with comments and blank lines removed and lines stripped), so
-    that a counter summary stays valid across edits of comments only."""
+    """Digest of the grid kernels' code (search_grid.hip, search_gemm.hip,
+    grid_index.h and awq_device.h with comments and blank lines removed and
+    lines stripped), so that a counter summary stays valid across edits of
+    comments only."""
     h = hashlib.sha256()
-    for f in ("search_grid.hip", "grid_index.h", "awq_device.h"):
+    for f in ("search_grid.hip", "search_gemm.hip", "grid_index.h", "awq_device.h"):
         src = open(os.path.join(ROOT, "post_bit_weight_awq_amd", "csrc", f)).read()
         src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
         src = re.sub(r"//[^\n]*", "", src)
         h.update("\n".join(ln.strip() for ln in src.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
+
+
+def uses_contraction(spec, cfg):
+    """Whether the search of this layer produces the weight error in its
+    preparation stage and contracts it (256 x 256 tiles)."""
+    import post_bit_weight_awq_amd as P
+    return P.awq_search_plan(spec.n_tokens, spec.in_features, spec.out_features,
+                             cfg).tile_out == 256
 
 
 def grid_kernel_names(layers, cfg):
@@ -85,7 +105,7 @@ def grid_kernel_names(layers, cfg):
     for L in layers:
         sp = L["spec"]
         plan = P.awq_search_plan(sp.n_tokens, sp.in_features, sp.out_features, cfg)
-        if plan.tile_out == 256:
+        if uses_contraction(sp, cfg):
             nm = "k_grid_gemm"
         else:
             nm = "k_grid_pp" if plan.tile_tokens in (512, 256) else "k_grid"
@@ -222,6 +242,22 @@ def cold_measurements(awq, cfg, layers, calib):
                                                  (ms_pack * 1e-3) / 1e9, 1),
                           "plain_read_of_X_gbs_cold": round(xb / (ms_read * 1e-3) / 1e9, 1),
                           "plain_read_of_W_gbs_cold": round(wb / (ms_read_w * 1e-3) / 1e9, 1)}
+    # the stage over the whole step, one event pair around its back-to-back
+    # calls (every input read once after the MALL clear), so the few
+    # microseconds an event adds between stages do not count against a stage
+    # of 10-50 us launches
+    res["_block"] = {
+        "stats_ms": timed(lambda: [awq.awq_act_stats(L["X"], out=L["sal"], workspace=L["sws"])
+                                   for L in layers]),
+        "pack_ms": timed(lambda: [awq.awq_pack(L["W"], L["s_best"], cfg, qweight=L["qw"],
+                                               step=L["st"], zero=L["zr"]) for L in layers]),
+        "plain_read_of_X_ms": timed(lambda: [calib.awq_calib_read(
+            L["X"].data_ptr(), L["X"].numel() * 2, sink.data_ptr(), 4096, stream)
+            for L in layers]),
+        "plain_read_of_W_ms": timed(lambda: [calib.awq_calib_read(
+            L["W"].data_ptr(), L["W"].numel() * 2, sink.data_ptr(), 4096, stream)
+            for L in layers]),
+    }
     del flush
     out_buf = torch.empty(1024 * 512, dtype=torch.float32, device="cuda")
     n_iter = 1024
@@ -597,8 +633,10 @@ def main():
     traffic = traffic_from_profiles(cfgspec.workload)
     calib = load_calib()
     measured = None
+    block_cold = None
     if calib is not None:
         cold, mfma_peak = cold_measurements(awq, cfg, layers, calib)
+        block_cold = cold.pop("_block")
         for name, v in cold.items():
             kernels[name].update(v)
         measured = {"mfma_f16_loop_tflops": mfma_peak,
@@ -614,12 +652,22 @@ def main():
         gbs = b / (ms * 1e-3) / 1e9
         r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
              "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": b,
-             "per_layer": {L["spec"].name: kernels[L["spec"].name][stage + "_gbs"]
-                           for L in layers}}
-        if all(plain_key in kernels[L["spec"].name] for L in layers):
+             "per_layer": {L["spec"].name: round(nbytes(L["spec"]) / (
+                 med(samples[stage][li]) * 1e-3) / 1e9, 1) for li, L in enumerate(layers)}}
+        if plain_key and all(plain_key in kernels[L["spec"].name] for L in layers):
             pr = {L["spec"].name: kernels[L["spec"].name][plain_key] for L in layers}
             r["plain_read_gbs_cold"] = pr
             r["frac_of_plain_read"] = {n: round(r["per_layer"][n] / pr[n], 3) for n in pr}
+        if block_cold is not None and stage + "_ms" in block_cold:
+            # the step's calls back to back after a MALL clear, one event pair
+            bg = b / (block_cold[stage + "_ms"] * 1e-3) / 1e9
+            src = "X" if stage == "stats" else "W"
+            rd = block_cold["plain_read_of_" + src + "_ms"]
+            rb = sum(L[src].numel() * 2 for L in layers)
+            r["back_to_back_cold"] = {
+                "achieved": round(bg, 1), "frac": round(bg / HBM_PEAK_GBS, 4),
+                "plain_read_gbs": round(rb / (rd * 1e-3) / 1e9, 1),
+                "frac_of_plain_read": round(bg / (rb / (rd * 1e-3) / 1e9), 3)}
         return r
 
     out = {
@@ -654,6 +702,9 @@ def main():
                          F[li] / (per["grid"][li] * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
                          for li, L in enumerate(layers)},
                      "stats": hbm_stage("stats", stats_bytes, "plain_read_of_X_gbs_cold"),
+                     **({"weight_error": hbm_stage(
+                         "prepare", lambda sp: weight_error_bytes(sp, cfg.n_grid), "")}
+                        if all(uses_contraction(L["spec"], cfg) for L in layers) else {}),
                      "pack": hbm_stage("pack", lambda sp: pack_bytes(sp, cfg.group_size),
                                        "plain_read_of_W_gbs_cold")},
         "kernels": kernels,

@@ -39,7 +39,10 @@ struct QuantSpec {
 // weight error of every grid point produced once by the preparation stage and
 // a plain contraction (search_gemm.hip).
 enum GridKernel { kGridFused = 0, kGridGemm = 1 };
-constexpr int64_t kGemmMinTokenTiles = 4;  // 256-token tiles for the contraction path
+// 256-token tiles for the contraction path: producing the weight error costs
+// a fixed 2 bytes per weight and grid point, which the faster contraction
+// repays from about 8 tiles (the 2048-token layers roughly break even)
+constexpr int64_t kGemmMinTokenTiles = 8;
 
 struct SearchPlan {
   int64_t tile_m, tile_n;        // tokens x outputs per tile
@@ -61,6 +64,7 @@ hipError_t launch_search(const void* X, const void* W, const float* sal, int64_t
 int grid_tile_m(int64_t n_tokens, int64_t out_features, int n_grid);
 void launch_grid_gemm(const void* X, const void* dW, double* partials, int64_t N, int64_t K,
                       int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream);
+int64_t grid_gemm_blocks(int64_t nt, int64_t no, int n_grid);
 void launch_grid(int tile_m, int group, const void* X, const void* W, const float* s_tab,
                  const float* inv_tab, const GroupParams* prm, double* partials, int64_t N,
                  int64_t K, int64_t OUT, int64_t nt, int64_t no, int n_grid, hipStream_t stream);

@@ -92,25 +92,40 @@ AWQ_HD uint32_t g_param_offset(int o0, int OUT, int prow0, int NT, int j) {
   return (uint32_t)(imin(o0 + prow0 + (NT / 4) * j, OUT - 1) - o0);
 }
 
-// ---- k_grid_gemm (8 wavefronts; 256 x 256 tiles of the materialized weight
+// ---- k_grid_gemm (8 wavefronts; 256 x 256 tiles of the produced weight
 // error, K steps of 64 columns, whole-line loads)
-// The j-th block an XCD receives (block b runs on XCD b % 8) takes token tile
-// j % nt of (grid point, output tile) pair 8 (j / nt) + xcd, pair index =
-// grid point * no + output tile: the token tiles of one pair run together on
-// one XCD and share its weight-error tile in that XCD's L2.
+// Blocks run on XCD b % 8.  The pairs (grid point, output tile), pair index =
+// grid point * no + output tile, are dealt to the XCDs (pair 8 m + xcd is the
+// XCD's m-th), and an XCD's j-th block takes a unit of its pairs in groups of
+// 4: group j / (4 nt), and within the group, runs of up to 8 token tiles
+// (the last run ragged) whose units go token tile fastest, so the 32 blocks
+// an XCD holds at a time share the group's weight-error tiles and the run's
+// activation tiles in its L2.  Every block has work, but for the last group's
+// units of a pair that an XCD lacks (when the pairs are not a multiple of 8):
+// idle blocks in a fixed pattern (runs padded to 8 tiles) loaded some shader
+// engines twice as much as others on layers of 5-7 token tiles.
 struct GemmUnit {
   int pair, ai, ot, tt, t0, o0;
 };
-AWQ_HD GemmUnit gemm_unit_of_block(int b, int nt, int no) {
-  GemmUnit r;
-  const int j = b >> 3;
-  r.pair = (j / nt) * 8 + (b & 7);
-  r.tt = j % nt;
-  r.ai = r.pair / no;
-  r.ot = r.pair - r.ai * no;
-  r.t0 = r.tt * 256;
-  r.o0 = r.ot * 256;
-  return r;
+constexpr int kGemmRunTiles = 8;    // token tiles per run
+constexpr int kGemmGroupPairs = 4;  // pairs per group
+AWQ_HD int gemm_blocks(int nt, int pairs) { return (pairs + 7) / 8 * nt * 8; }
+AWQ_HD GemmUnit gemm_unit_of_block(int b, int nt, int no, int pairs) {
+  constexpr int T = kGemmRunTiles, P = kGemmGroupPairs;
+  const int j = b >> 3, ppx = (pairs + 7) / 8;
+  const int g = j / (P * nt), q = j - g * P * nt;
+  const int pc = imin(P, ppx - g * P);  // pairs of this group
+  const int tb = q / (pc * T), r = q - tb * pc * T;
+  const int tc = imin(T, nt - tb * T);  // token tiles of this run
+  const int p = r / tc;
+  GemmUnit u;
+  u.tt = tb * T + (r - p * tc);
+  u.pair = (g * P + p) * 8 + (b & 7);
+  u.ai = u.pair / no;
+  u.ot = u.pair - u.ai * no;
+  u.t0 = u.tt * 256;
+  u.o0 = u.ot * 256;
+  return u;
 }
 // Byte offset, from the first row of a 256-row tile, of the lane's 16-byte
 // piece of load i of wavefront w (8 rows x 128 bytes per load, row r of the

@@ -278,8 +278,9 @@ k_group_params(const _Float16* __restrict__ W, const float* __restrict__ s_tab,
 
 // -------------------------------------------------------------------- argmin
 // 1024 threads: wavefront w sums the partials of grid points w, w+16, ... in
-// a fixed order (lane-strided, then a shuffle tree), so the losses are
-// bitwise reproducible.  Wavefront 0 then picks the first minimum.
+// a fixed order (lane-strided with eight loads in flight, then a shuffle
+// tree), so the losses are bitwise reproducible.  Wavefront 0 then picks the
+// first minimum.
 constexpr int kArgminThreads = 1024;
 
 __global__ void __launch_bounds__(kArgminThreads)
@@ -290,8 +291,17 @@ k_argmin(const double* __restrict__ partials, int64_t n_tiles, int n_grid, doubl
   __shared__ int best_sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = wave; i < n_grid; i += kArgminThreads / kWave) {
+    const double* pp = partials + (int64_t)i * n_tiles;
     double acc = 0.0;
-    for (int64_t t = lane; t < n_tiles; t += kWave) acc += partials[(int64_t)i * n_tiles + t];
+    int64_t t = lane;
+    for (; t + 7 * kWave < n_tiles; t += 8 * kWave) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pp[t + kWave * u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; t < n_tiles; t += kWave) acc += pp[t];
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) acc += __shfl_xor(acc, d, kWave);
     if (lane == 0) lsh[i] = acc / count;
@@ -344,7 +354,7 @@ SearchPlan search_plan(int64_t n_tokens, int64_t in_features, int64_t out_featur
     p.tile_n = 256;
     p.n_t_tiles = (n_tokens + 255) / 256;
     p.n_o_tiles = (out_features + 255) / 256;
-    p.grid_blocks = ((int64_t)n_grid * p.n_o_tiles + 7) / 8 * 8 * p.n_t_tiles;
+    p.grid_blocks = grid_gemm_blocks(p.n_t_tiles, p.n_o_tiles, n_grid);
   } else {
     p.kernel = kGridFused;
     p.tile_m = grid_tile_m(n_tokens, out_features, n_grid);

@@ -186,15 +186,24 @@ static void check_gemm_tile(int t0, int o0, int64_t N, int64_t K, int64_t OUT) {
 
 // every (pair, token tile) of the contraction launch is taken by exactly one
 // block that passes the early return, with its tile inside the layer
+static int64_t gemm_blocks64(int64_t nt, int64_t pairs) { return cdiv(pairs, 8) * nt * 8; }
+
 static void check_gemm_units(int64_t N, int64_t OUT, int n_grid, bool all) {
   const int64_t nt = cdiv(N, 256), no = cdiv(OUT, 128 * 2), pairs = n_grid * no;
-  const int64_t blocks = cdiv(pairs, 8) * 8 * nt;
+  const int64_t blocks = gemm_blocks64(nt, pairs);
+  CHECK(blocks == gemm_blocks((int)nt, (int)pairs), "gemm block count");
   std::vector<uint8_t> seen;
   if (all) seen.assign((size_t)(pairs * nt), 0);
   for (int64_t b = 0; b < blocks; ++b) {
     if (!all && b >= 4096 && b < blocks - 4096) b = blocks - 4096;
-    const GemmUnit un = gemm_unit_of_block((int)b, (int)nt, (int)no);
-    if (un.pair >= pairs) continue;
+    const GemmUnit un = gemm_unit_of_block((int)b, (int)nt, (int)no, (int)pairs);
+    CHECK(un.tt >= 0 && un.tt < nt, "gemm token tile of block %lld", (long long)b);
+    if (un.pair >= pairs) {
+      // idle blocks only in the last group of 4 pairs (XCDs with a pair fewer)
+      const int64_t ppx = cdiv(pairs, 8), first_last = (ppx - 1) / 4 * 4 * nt;
+      CHECK(b / 8 >= first_last, "gemm idle block %lld before the last group", (long long)b);
+      continue;
+    }
     CHECK(un.ai >= 0 && un.ai < n_grid && un.ot >= 0 && un.ot < no && un.tt >= 0 && un.tt < nt,
           "gemm unit %lld", (long long)b);
     CHECK(un.t0 < N && un.o0 < OUT, "gemm tile origin");
@@ -211,7 +220,8 @@ static void check_gemm_units(int64_t N, int64_t OUT, int n_grid, bool all) {
 int main() {
   const int64_t MAXT = (int64_t)1 << 24, MAXF = (int64_t)1 << 20, MAXW = (int64_t)1 << 34;
   const int64_t MAXBLOCKS = (int64_t)1 << 23;
-  const int64_t Ns[] = {1, 127, 128, 129, 255, 256, 257, 511, 512, 513, 4096, MAXT - 1, MAXT};
+  const int64_t Ns[] = {1, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1793, 2048, 2049, 3000,
+                        4096, MAXT - 1, MAXT};
   const int64_t Ks[] = {128, 4096, 13824, MAXF / 2, MAXF};
   const int64_t OUTs[] = {1, 127, 128, 129, 27648, (int64_t)1 << 14, MAXF};
   const int grids[] = {1, 20, 64};
@@ -263,19 +273,27 @@ int main() {
             }
           }
       }
-  // the contraction path (layers of at least four 256-token tiles)
+  // the contraction path (layers of at least eight 256-token tiles)
   for (int64_t N : Ns)
     for (int64_t K : Ks)
       for (int64_t OUT : OUTs) {
-        if (OUT * K > MAXW || N < 769) continue;
+        if (OUT * K > MAXW || N < 1793) continue;
         for (int n_grid : grids) {
           const int64_t nt = cdiv(N, 256), no = cdiv(OUT, 256);
-          if (cdiv(n_grid * no, 8) * 8 * nt > MAXBLOCKS) continue;
+          if (gemm_blocks64(nt, n_grid * no) > MAXBLOCKS) continue;
           ++shapes;
           for (int64_t tt : {(int64_t)0, nt - 1})
             for (int64_t ot : {(int64_t)0, no - 1}) check_gemm_tile((int)(tt * 256), (int)(ot * 256), N, K, OUT);
           check_gemm_units(N, OUT, n_grid, n_grid * no * nt <= ((int64_t)1 << 20));
         }
+      }
+  // the contraction's block order on its own, for any token-tile count (whole
+  // and ragged runs of 8 tiles, whole and ragged groups of 4 pairs)
+  for (int64_t nt = 1; nt <= 40; ++nt)
+    for (int64_t OUT : {(int64_t)1, (int64_t)256, (int64_t)700, (int64_t)5120, (int64_t)15360})
+      for (int n_grid : {1, 3, 7, 20, 33}) {
+        ++shapes;
+        check_gemm_units(nt * 256 - (nt % 3) * 50, OUT, n_grid, true);
       }
   if (fails) {
     printf("%d violations over %d shapes\n", fails, shapes);

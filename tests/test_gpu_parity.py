@@ -394,13 +394,14 @@ def test_explicit_stream_argument(awq):
 
 
 # ------------------------- layers of many token tiles: the contraction path
-# At least four 256-token tiles: the preparation stage writes every grid
+# At least eight 256-token tiles: the preparation stage writes every grid
 # point's weight error dW_i = fp16(Wq_i - W) once and the grid stage contracts
-# it (tiles of 256 tokens x 256 outputs).
+# it (tiles of 256 tokens x 256 outputs; rounds of 4 pairs x 8 token tiles).
 GEMM_CASES = [
-    ("ragged", dict(n=1000, k=384, o=300)),     # last token tile 232 rows, last output tile 44
-    ("exact", dict(n=1024, k=256, o=512)),
-    ("wide_k", dict(n=800, k=11008, o=257)),    # 86 column groups of 128; ragged outputs
+    ("ragged", dict(n=2000, k=384, o=300)),     # last token tile 208 rows, last output tile 44
+    ("exact", dict(n=2048, k=256, o=512)),
+    ("nine_tiles", dict(n=2100, k=256, o=700)),  # a second round with one token tile
+    ("wide_k", dict(n=1800, k=11008, o=257)),   # 86 column groups of 128; ragged outputs
 ]
 
 
@@ -425,7 +426,7 @@ def test_search_contraction_path_matches_oracle(awq, name, shape):
 @pytest.mark.parametrize("group,w_bit,zp", [(64, 4, True), (32, 4, True), (128, 3, True),
                                             (128, 4, False), (32, 3, False)])
 def test_search_contraction_path_quantizer_variants(awq, group, w_bit, zp):
-    n, k, o = 1061, 512, 260
+    n, k, o = 2061, 512, 260
     _say(f"contraction path variant g{group} b{w_bit} zp{zp}")
     _, X, W = synth.make_custom(n, k, o, seed=group + w_bit, token_scale=True)
     Xd, Wd = dev(X), dev(W)
@@ -449,7 +450,7 @@ def test_contraction_weight_error_matches_oracle(awq, group, w_bit, zp):
     near a tie, so its codes are the oracle's; the rule for codes decided at
     a .5 tie would still admit differences only there (at most 1e-6 of the
     elements, each one code), and none occurs."""
-    n, k, o = 1024, 384, 300
+    n, k, o = 2048, 384, 300
     _say(f"contraction weight error {n}x{k}->{o} g{group} b{w_bit} zp{zp}")
     _, X, W = synth.make_custom(n, k, o, seed=5, token_scale=True)
     Xd, Wd = dev(X), dev(W)
@@ -481,7 +482,7 @@ def test_contraction_weight_error_matches_oracle(awq, group, w_bit, zp):
 def test_contraction_grid_stage_repeated(awq):
     """Grid and select stages rerun on one prepared workspace give bitwise the
     same losses (fixed per-tile partial slots, fixed-order sums)."""
-    n, k, o = 1100, 512, 600
+    n, k, o = 2100, 512, 600
     _, X, W = synth.make_custom(n, k, o, seed=9)
     Xd, Wd, sal, res = run_layer(awq, X, W)
     assert res.plan.tile_tokens == 256
@@ -497,7 +498,7 @@ def test_contraction_path_replays_in_a_hip_graph(awq):
     """Statistics, the contraction-path search and pack captured in one HIP
     graph and replayed with eager work between replays: every replay equals
     the eager run bit for bit."""
-    _, X, W = synth.make_custom(1024, 512, 512, seed=13)
+    _, X, W = synth.make_custom(2048, 512, 512, seed=13)
     Xd, Wd = dev(X), dev(W)
 
     def run():
