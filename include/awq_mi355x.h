@@ -150,8 +150,13 @@ int awq_act_stats_noalloc(const void* X, int64_t n_tokens, int64_t in_features, 
  *   (the floor keeps a NaN), so every grid point above 0 has a NaN loss.
  *   in_features must be a multiple of 128; n_tokens, out_features >= 1.
  * The workspace (size from awq_search_workspace_size) holds the scale table,
- * the per-group quantizer parameters and the per-tile partial sums;
- * awq_search_plan describes where.  The squared output error is formed as
+ * the per-tile partial sums and either the per-group quantizer parameters
+ * (layers of at most four 256-token tiles: a fused kernel quantizes,
+ * dequantizes and contracts per tile of 512, 256 or 128 tokens x 128 outputs)
+ * or, for more tokens, the fp16 weight error of every grid point,
+ * 2 * n_grid * out_features * in_features bytes (produced once, then
+ * contracted on tiles of 256 tokens x 256 outputs); awq_search_plan describes
+ * the tiling and where the partials and scales are.  The squared output error is formed as
  * (X (Wq - W)^T)^2 with the weight error rounded once to fp16 (the same
  * quantity as (X Wq^T - X W^T)^2 up to that rounding), so no reference output
  * is stored.
@@ -184,10 +189,13 @@ int awq_search_layer(const void* X, const void* W, const float* sal, int64_t n_t
  * awq_search_layer(...) equals awq_search_layer_stages(AWQ_STAGE_ALL, ...).
  * A stage reads what the earlier stages left in the workspace, so the stages of
  * one search must run in order, on one workspace, with the same arguments.
- *   AWQ_STAGE_PREPARE: scale table and the per-group quantizer parameters of
- *                      every grid point (no reference output is formed)
- *   AWQ_STAGE_GRID:    the fused quantize-dequantize + MFMA contraction +
- *                      squared-error kernel over all grid points
+ *   AWQ_STAGE_PREPARE: scale table and, for every grid point, the per-group
+ *                      quantizer parameters or (more than four 256-token
+ *                      tiles) the fp16 weight error (no reference output is
+ *                      formed)
+ *   AWQ_STAGE_GRID:    the MFMA contraction and squared errors of all grid
+ *                      points (fused with the quantize-dequantize work on
+ *                      layers of at most four token tiles)
  *   AWQ_STAGE_SELECT:  losses, argmin and s_best */
 #define AWQ_STAGE_PREPARE 1
 #define AWQ_STAGE_GRID 2

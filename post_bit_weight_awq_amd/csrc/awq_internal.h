@@ -39,10 +39,12 @@ struct QuantSpec {
 // weight error of every grid point produced once by the preparation stage and
 // a plain contraction (search_gemm.hip).
 enum GridKernel { kGridFused = 0, kGridGemm = 1 };
-// 256-token tiles for the contraction path: producing the weight error costs
-// a fixed 2 bytes per weight and grid point, which the faster contraction
-// repays from about 8 tiles (the 2048-token layers roughly break even)
-constexpr int64_t kGemmMinTokenTiles = 8;
+// 256-token tiles from which the contraction path runs.  Producing the weight
+// error costs a fixed 2 bytes per weight and grid point; measured on 4096- to
+// 13824-wide layers, the fused kernels win up to 1024 tokens when the tokens
+// fill their 512-token tiles (512 and 1024 tokens: 7-32 %), the contraction
+// from 1152 tokens on (2-20 %)
+constexpr int64_t kGemmMinTokenTiles = 5;
 
 struct SearchPlan {
   int64_t tile_m, tile_n;        // tokens x outputs per tile

@@ -220,8 +220,8 @@ static void check_gemm_units(int64_t N, int64_t OUT, int n_grid, bool all) {
 int main() {
   const int64_t MAXT = (int64_t)1 << 24, MAXF = (int64_t)1 << 20, MAXW = (int64_t)1 << 34;
   const int64_t MAXBLOCKS = (int64_t)1 << 23;
-  const int64_t Ns[] = {1, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1793, 2048, 2049, 3000,
-                        4096, MAXT - 1, MAXT};
+  const int64_t Ns[] = {1, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1024, 1025, 1500, 2048,
+                        2049, 3000, 4096, MAXT - 1, MAXT};
   const int64_t Ks[] = {128, 4096, 13824, MAXF / 2, MAXF};
   const int64_t OUTs[] = {1, 127, 128, 129, 27648, (int64_t)1 << 14, MAXF};
   const int grids[] = {1, 20, 64};
@@ -273,11 +273,11 @@ int main() {
             }
           }
       }
-  // the contraction path (layers of at least eight 256-token tiles)
+  // the contraction path (layers of at least five 256-token tiles)
   for (int64_t N : Ns)
     for (int64_t K : Ks)
       for (int64_t OUT : OUTs) {
-        if (OUT * K > MAXW || N < 1793) continue;
+        if (OUT * K > MAXW || N < 1025) continue;
         for (int n_grid : grids) {
           const int64_t nt = cdiv(N, 256), no = cdiv(OUT, 256);
           if (gemm_blocks64(nt, n_grid * no) > MAXBLOCKS) continue;

@@ -109,17 +109,17 @@ def test_search_workspace_too_small(lib):
     assert rc == _lib.AWQ_ERR_WORKSPACE
 
 
-@pytest.mark.parametrize("n", [500, 1792, 1793, 4096])
+@pytest.mark.parametrize("n", [500, 1024, 1025, 4096])
 def test_search_plan_layout(lib, n):
-    # up to 1792 tokens (seven 256-token tiles): the fused grid kernel and its
-    # parameter table; from 1793 (eight tiles): the contraction path and its
+    # up to 1024 tokens (four 256-token tiles): the fused grid kernel and its
+    # parameter table; from 1025 (five tiles): the contraction path and its
     # weight error
     cfg = _cfg(lib)
     plan = _lib.AwqSearchPlan()
     assert lib.awq_search_plan_query(n, 4096, 1000, ctypes.byref(cfg), ctypes.byref(plan)) == 0
     assert plan.n_token_tiles == -(-n // plan.tile_tokens)
     assert plan.n_out_tiles == -(-1000 // plan.tile_out)
-    contraction = n >= 1793
+    contraction = n >= 1025
     assert (plan.tile_tokens, plan.tile_out) == ((256, 256) if contraction else
                                                  (plan.tile_tokens, 128))
     regions = sorted([

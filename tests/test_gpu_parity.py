@@ -264,7 +264,7 @@ def test_search_split_last_round(awq, n, k, o):
     _say(f"search split last round {n}x{k}->{o}")
     _, X, W = synth.make_custom(n, k, o, seed=n + o)
     Xd, Wd, sal, res = run_layer(awq, X, W)
-    assert res.plan.tile_out == 128  # the fused kernels (fewer than four 256-token tiles)
+    assert res.plan.tile_out == 128  # the fused kernels (at most four 256-token tiles)
     ref = O.search_layer(X, W, host(sal))
     losses = host(res.losses)
     rel = np.abs(losses - ref.losses) / ref.losses
@@ -394,13 +394,15 @@ def test_explicit_stream_argument(awq):
 
 
 # ------------------------- layers of many token tiles: the contraction path
-# At least eight 256-token tiles: the preparation stage writes every grid
+# At least five 256-token tiles: the preparation stage writes every grid
 # point's weight error dW_i = fp16(Wq_i - W) once and the grid stage contracts
-# it (tiles of 256 tokens x 256 outputs; rounds of 4 pairs x 8 token tiles).
+# it (tiles of 256 tokens x 256 outputs; groups of 4 pairs, runs of up to 8
+# token tiles).
 GEMM_CASES = [
     ("ragged", dict(n=2000, k=384, o=300)),     # last token tile 208 rows, last output tile 44
     ("exact", dict(n=2048, k=256, o=512)),
-    ("nine_tiles", dict(n=2100, k=256, o=700)),  # a second round with one token tile
+    ("nine_tiles", dict(n=2100, k=256, o=700)),  # a second run of one token tile
+    ("five_tiles", dict(n=1100, k=512, o=1300)),  # one run of five tiles; last group of 3 pairs
     ("wide_k", dict(n=1800, k=11008, o=257)),   # 86 column groups of 128; ragged outputs
 ]
 
