@@ -291,7 +291,7 @@ int main() {
   // and ragged runs of 8 tiles, whole and ragged groups of 4 pairs)
   for (int64_t nt = 1; nt <= 40; ++nt)
     for (int64_t OUT : {(int64_t)1, (int64_t)256, (int64_t)700, (int64_t)5120, (int64_t)15360})
-      for (int n_grid : {1, 3, 7, 20, 33}) {
+      for (int n_grid : {1, 3, 7, 20, 33, 64}) {
         ++shapes;
         check_gemm_units(nt * 256 - (nt % 3) * 50, OUT, n_grid, true);
       }

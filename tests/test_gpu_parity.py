@@ -425,6 +425,24 @@ def test_search_contraction_path_matches_oracle(awq, name, shape):
     assert np.array_equal(host(res.s_best).view(np.uint32), ref.s[best].view(np.uint32))
 
 
+@pytest.mark.parametrize("n,k,o,n_grid", [(1025, 128, 1, 20), (1300, 128, 3, 1),
+                                          (1100, 256, 129, 64), (4097, 128, 2, 3)])
+def test_search_contraction_path_edge_shapes(awq, n, k, o, n_grid):
+    """The contraction path at its edges: one output row, two 64-column K
+    steps, a last token tile of one row (1025 and 4097 tokens), 1 and 64 grid
+    points (the weight error of every grid point in the workspace)."""
+    _say(f"contraction edge {n}x{k}->{o} grid {n_grid}")
+    _, X, W = synth.make_custom(n, k, o, seed=n + k + o + n_grid)
+    Xd, Wd, sal, res = run_layer(awq, X, W, n_grid=n_grid)
+    assert (res.plan.tile_tokens, res.plan.tile_out) == (256, 256)
+    ref = O.search_layer(X, W, host(sal), n_grid=n_grid)
+    losses = host(res.losses)
+    rel = np.abs(losses - ref.losses) / ref.losses
+    _say(f"  max rel loss diff {rel.max():.3e}")
+    assert np.all(rel <= LOSS_RTOL)
+    check_best(int(host(res.best_idx)[0]), ref.losses)
+
+
 @pytest.mark.parametrize("group,w_bit,zp", [(64, 4, True), (32, 4, True), (128, 3, True),
                                             (128, 4, False), (32, 3, False)])
 def test_search_contraction_path_quantizer_variants(awq, group, w_bit, zp):
