@@ -148,11 +148,13 @@ def cpu_baseline(cfg_key, target_s):
     t_stats = t_search = t_pack = 0.0
     flops = 0.0
     parts = []
+    per_layer = []
     for li, spec in enumerate(layers):
         _, X, W = synth.make_layer(cfg_key, li)
         t0 = time.perf_counter()
         sal = O.act_stats(X)
-        t_stats += time.perf_counter() - t0
+        ts = time.perf_counter() - t0
+        t_stats += ts
         # size the row cut from a probe of one grid point on 512 rows (smaller
         # probes are dominated by per-call costs and undersize the cut)
         rows = min(512, spec.out_features)
@@ -165,13 +167,17 @@ def cpu_baseline(cfg_key, target_s):
         del W
         t0 = time.perf_counter()
         res = O.search_layer(X, Wc, sal)
-        t_search += time.perf_counter() - t0
+        tq = time.perf_counter() - t0
+        t_search += tq
         t0 = time.perf_counter()
         O.pack(Wc, res.s_best)
-        t_pack += time.perf_counter() - t0
+        tp = time.perf_counter() - t0
+        t_pack += tp
         flops += 2.0 * 20 * spec.n_tokens * spec.in_features * rows
         parts.append(f"{spec.name} {spec.n_tokens}x{spec.in_features}: {rows} of "
                      f"{spec.out_features} rows")
+        per_layer.append({"layer": spec.name, "rows": rows, "stats_s": round(ts, 3),
+                          "search_s": round(tq, 3), "pack_s": round(tp, 3)})
     return {
         "value": flops / (t_stats + t_search + t_pack) / 1e12,
         "unit": "TFLOP/s",
@@ -181,6 +187,8 @@ def cpu_baseline(cfg_key, target_s):
                    f"over all tokens, 20-point search and pack on a leading cut of output rows ("
                    + "; ".join(parts) + ")"),
         "seconds": {"stats": t_stats, "search": t_search, "pack": t_pack},
+        "per_layer": per_layer,
+        "host": {"affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": int(threads)},
     }
 
 
