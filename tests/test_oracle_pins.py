@@ -690,10 +690,62 @@ def test_w4a16_abs_matmul_matches_exact_rationals_and_bounds_the_product():
 @pytest.mark.parametrize("mutation", ["floor_round", "symmetric_step", "grid_to_one",
                                       "no_zero_canon", "nibble_order", "fold_multiplies",
                                       "abs_bound_drops_zero", "tie_exact_only",
-                                      "stats_nan_ignored"])
+                                      "stats_nan_ignored", "no_unscale", "loss_over_tokens_only",
+                                      "argmin_last", "stats_over_features", "no_floor",
+                                      "pow_in_binary32"])
 def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
     """Each plausible slip in the oracle trips at least one pin above."""
-    if mutation == "floor_round":
+    if mutation == "no_unscale":
+        # the quantized scaled weight is not divided by s again
+        orig = O.dequantize
+        monkeypatch.setattr(O, "dequantize", lambda gq, inv_s_row, group=128, literal_div=None:
+                            orig(gq, np.ones_like(np.asarray(inv_s_row, F32)), group, literal_div))
+        with pytest.raises(AssertionError):
+            test_scaling_identity_is_exact_when_rounding_is_exact()
+    elif mutation == "loss_over_tokens_only":
+        # the squared error averaged over tokens but summed over outputs
+        orig = O.search_layer
+
+        def per_token(X, W, sal, *a, **kw):
+            r = orig(X, W, sal, *a, **kw)
+            r.losses = r.losses * np.asarray(W).shape[0]
+            return r
+        monkeypatch.setattr(O, "search_layer", per_token)
+        with pytest.raises(AssertionError):
+            test_losses_match_exact_rationals(3)
+    elif mutation == "argmin_last":
+        def last(losses):
+            best, best_i = np.inf, -1
+            for i, v in enumerate(np.asarray(losses, dtype=F64)):
+                if v <= best:
+                    best, best_i = v, i
+            if best_i < 0:
+                raise O.NonFiniteLosses("no finite loss on the grid")
+            return best_i
+        monkeypatch.setattr(O, "argmin_first", last)
+        with pytest.raises(AssertionError):
+            test_argmin_rules()
+    elif mutation == "stats_over_features":
+        # the mean taken along the wrong axis (per token instead of per channel)
+        orig = O.act_stats
+        monkeypatch.setattr(O, "act_stats", lambda X: orig(np.ascontiguousarray(np.asarray(X).T)))
+        with pytest.raises((AssertionError, IndexError)):
+            test_stats_exact_mean_then_two_roundings()
+    elif mutation == "no_floor":
+        orig = O.scale_table
+        monkeypatch.setattr(O, "scale_table", lambda sal, n_grid=20, floor=None:
+                            orig(sal, n_grid, 0.0))
+        with pytest.raises(AssertionError):
+            test_scale_table_against_high_precision_pow()
+    elif mutation == "pow_in_binary32":
+        def pow32(sal, n_grid=20, floor=O.SAL_FLOOR):
+            base = np.maximum(np.asarray(sal, F32), F32(floor))
+            s = np.power(base[None, :], O.alphas(n_grid).astype(F32)[:, None]).astype(F32)
+            return s, (F32(1.0) / s).astype(F32)
+        monkeypatch.setattr(O, "scale_table", pow32)
+        with pytest.raises(AssertionError):
+            test_scale_table_against_high_precision_pow()
+    elif mutation == "floor_round":
         monkeypatch.setattr(O.np, "rint", np.floor)
         with pytest.raises(AssertionError):
             test_quantizer_matches_exact_rational_emulation(0)
