@@ -21,9 +21,16 @@
 // with fp32 accumulators in registers for the whole K loop.  K steps of 64
 // columns: both operand tiles (256 rows x 128 bytes each) move into LDS by
 // direct loads of 8 rows x 128 bytes per instruction (16-byte piece p of row
-// r stored at p ^ (r & 7), so the fragment reads hit every bank once),
-// double-buffered, one barrier per step.  A step reads both 32-column halves'
-// fragments first, then issues their 64 MFMAs.  Rows past the last token or
+// r stored at p ^ (r & 7), so the fragment reads hit every bank once), one
+// barrier per step.  The weight-error tile has two LDS stages and is loaded
+// for step s + 1 at the start of step s; the activation tile has three and is
+// loaded for step s + 2 at the end of step s, after the MFMAs are issued and
+// before the barrier, where a wavefront would otherwise wait (160 KB of LDS).
+// The load instructions stall the wavefront that issues them; moving half of
+// them out of the step's start ran 0.5-2.6 % faster on the 13B shapes, where
+// a third activation stage loaded at the start lost 3-5 %.  A step reads both
+// 32-column halves' fragments first, then issues their 64 MFMAs.  Rows past
+// the last token or
 // output re-read the last row and are masked in the epilogue.  Each tile
 // writes its sum of squares (fp32 per lane, fp64 across the block) to its
 // grid point's partial slot.  Block order: the 32 blocks an XCD holds at a
@@ -39,6 +46,7 @@ namespace awq {
 
 constexpr int kGemmBM = 256, kGemmBN = 256, kGemmKC = 64;
 constexpr int kGemmWM = 4, kGemmWN = 2;  // wavefront grid (tokens x outputs)
+constexpr int kGemmXS = 3, kGemmWS = 2;  // LDS stages: activations, weight error
 
 __global__ void __launch_bounds__(512, 1)
 k_grid_gemm(const _Float16* __restrict__ X, const _Float16* __restrict__ dW,
@@ -47,9 +55,13 @@ k_grid_gemm(const _Float16* __restrict__ X, const _Float16* __restrict__ dW,
   constexpr int TM = kGemmBM / kGemmWM, TN = kGemmBN / kGemmWN;  // 64 x 128 per wavefront
   constexpr int MT = TM / 16, NT = TN / 16;
   constexpr int LOADS = kGemmBM * KC * 2 / 1024 / 8;  // per operand, wavefront and step
-  __shared__ __attribute__((aligned(16))) _Float16 sa[2][kGemmBM * KC];
-  __shared__ __attribute__((aligned(16))) _Float16 sb[2][kGemmBN * KC];
-  __shared__ double red[8];
+  static_assert(LOADS == 4, "the loop's vmcnt(4) counts one step's activation loads");
+  constexpr int XS = kGemmXS, WS = kGemmWS;
+  // all of the LDS: XS activation stages, then WS weight-error stages; the
+  // epilogue's 8 partial sums reuse its start once the loop is done
+  __shared__ __attribute__((aligned(16))) _Float16 lds[(XS * kGemmBM + WS * kGemmBN) * KC];
+  _Float16* const sa = lds;
+  _Float16* const sb = lds + XS * kGemmBM * KC;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kGemmWN, wn = wave % kGemmWN;
@@ -70,13 +82,18 @@ k_grid_gemm(const _Float16* __restrict__ X, const _Float16* __restrict__ dW,
                  : "v"(off), "s"(base), "s"(la)
                  : "memory", "m0");
   };
-  auto load_step = [&](int s, int buf) {
+  // step s's tiles go to stage s % XS (activations) and s % WS (weight error)
+  auto load_x = [&](int s) {
     const _Float16* pa = xa + s * KC;
+    _Float16* d = sa + (s % XS) * kGemmBM * KC;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) dma(pa, oa[i], d + (wave * LOADS + i) * 8 * KC);
+  };
+  auto load_w = [&](int s) {
     const _Float16* pb = xb + s * KC;
+    _Float16* d = sb + (s % WS) * kGemmBN * KC;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) dma(pa, oa[i], &sa[buf][(wave * LOADS + i) * 8 * KC]);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) dma(pb, ob[i], &sb[buf][(wave * LOADS + i) * 8 * KC]);
+    for (int i = 0; i < LOADS; ++i) dma(pb, ob[i], d + (wave * LOADS + i) * 8 * KC);
   };
   // the lane's 16 bytes of a 16-row fragment: row (lane % 16), k half kh,
   // 8-column piece 4 kh + lane / 16 of the step
@@ -90,22 +107,27 @@ k_grid_gemm(const _Float16* __restrict__ X, const _Float16* __restrict__ dW,
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[m][n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int nk = K / KC;
-  load_step(0, 0);
+  const int nk = K / KC;  // K is a multiple of 128, so nk >= 2
+  load_x(0);
+  load_x(1);
+  load_w(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   __syncthreads();
   half8 a0[MT], b0[NT], a1[MT], b1[NT];
   for (int s = 0; s < nk; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nk) load_step(s + 1, buf ^ 1);
+    // the weight-error stage of step s + 1 last held step s - 1, which every
+    // wavefront finished reading before the previous barrier
+    if (s + 1 < nk) load_w(s + 1);
+    const _Float16* ta = sa + (s % XS) * kGemmBM * KC;
+    const _Float16* tb = sb + (s % WS) * kGemmBN * KC;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) a0[m] = frag(sa[buf], wm * TM + m * 16 + (lane & 15), 0);
+    for (int m = 0; m < MT; ++m) a0[m] = frag(ta, wm * TM + m * 16 + (lane & 15), 0);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) b0[n] = frag(sb[buf], wn * TN + n * 16 + (lane & 15), 0);
+    for (int n = 0; n < NT; ++n) b0[n] = frag(tb, wn * TN + n * 16 + (lane & 15), 0);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) a1[m] = frag(sa[buf], wm * TM + m * 16 + (lane & 15), 1);
+    for (int m = 0; m < MT; ++m) a1[m] = frag(ta, wm * TM + m * 16 + (lane & 15), 1);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) b1[n] = frag(sb[buf], wn * TN + n * 16 + (lane & 15), 1);
+    for (int n = 0; n < NT; ++n) b1[n] = frag(tb, wn * TN + n * 16 + (lane & 15), 1);
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -116,9 +138,21 @@ k_grid_gemm(const _Float16* __restrict__ X, const _Float16* __restrict__ dW,
 #pragma unroll
       for (int n = 0; n < NT; ++n)
         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[m], b1[n], acc[m][n], 0, 0, 0);
-    // the next step's operands have landed (this wavefront's loads), and no
-    // wavefront still reads this step's buffers (the barrier)
-    __builtin_amdgcn_s_waitcnt(0x0f70);
+    // the activation stage of step s + 2 also last held step s - 1; its loads
+    // go out after this step's MFMAs (the scheduling barrier keeps them there)
+    const bool more = s + 2 < nk;
+    if (more) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(s + 2);
+    }
+    // step s + 1's tiles have landed (this wavefront's loads: the weight error
+    // issued this step, the activations last step; the activation loads just
+    // issued, the last 4, may stay in flight), and no wavefront still reads
+    // this step's stages (the barrier)
+    if (more)
+      __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
   }
 
@@ -140,6 +174,7 @@ k_grid_gemm(const _Float16* __restrict__ X, const _Float16* __restrict__ dW,
   double dsum = (double)sq;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) dsum += __shfl_xor(dsum, d, kWave);
+  double* const red = (double*)lds;  // the loop's last barrier ended every read and load
   if (lane == 0) red[wave] = dsum;
   __syncthreads();
   if (tid == 0) {
