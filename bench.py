@@ -652,9 +652,11 @@ def main():
                             "wavefront shape; *_cold: MALL cleared by a 512 MiB read first"}
 
     def hbm_stage(stage, nbytes, plain_key):
-        """Bytes of the stage over all layers / the sum of its median launch
-        times, against the HBM peak and against a plain streaming read of the
-        same input (cold, same size) where one was measured."""
+        """Bytes of the stage over all layers / the sum of its median times in
+        the timed steps, against the HBM peak and against a plain streaming
+        read of the same input (cold, same size) where one was measured; for
+        stats and pack also the step's calls timed back to back after a MALL
+        clear (one event pair, so no between-stage event time is counted)."""
         b = sum(nbytes(L["spec"]) for L in layers)
         ms = sum(med(samples[stage][li]) for li in range(len(layers)))
         gbs = b / (ms * 1e-3) / 1e9
