@@ -1,5 +1,7 @@
-// The fused grid kernel of the AWQ search: for one (grid point i, token tile,
-// output tile) it quantizes and dequantizes the weight tile of W diag(s_i)
+// The fused grid kernels of the AWQ search, for layers of at most four
+// 256-token tiles (layers of more tokens produce the weight error once and
+// contract it: search_gemm.hip): for one (grid point i, token tile, output
+// tile) a block quantizes and dequantizes the weight tile of W diag(s_i)
 // (asymmetric INT4, groups of 128; "AWQ > Salient Weight Preservation",
 // step-size equation), divides it by s_i again (dev.to "AWQ: How
 // Activation-Aware Quantization Saves 4-bit LLMs", search_scale listing),
