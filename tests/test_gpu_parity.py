@@ -339,15 +339,21 @@ def test_stats_non_finite(awq, n, k):
     assert np.array_equal(sal[fin].view(np.uint32), ref[fin].view(np.uint32))
 
 
-def test_search_non_finite_saliency(awq):
-    """A NaN and an infinite saliency (finite X): the scale table follows the
-    oracle's floor-then-power (alpha = 0 still gives s = 1, other grid points
-    NaN or inf), bit for bit; every grid point above 0 has a NaN loss on both
-    sides, and the search keeps alpha = 0."""
-    _, X, W = synth.make_layer(1, 0, n_tokens=64, out_features=64)
+@pytest.mark.parametrize("n_tokens", [64, 1100])
+@pytest.mark.parametrize("kind", ["nan", "inf", "both"])
+def test_search_non_finite_saliency(awq, n_tokens, kind):
+    """A NaN and/or an infinite saliency (finite X), on the fused path (64
+    tokens) and the contraction path (1100 tokens): the scale table follows
+    the oracle's floor-then-power (alpha = 0 still gives s = 1, other grid
+    points NaN or inf), bit for bit; every grid point above 0 has a NaN loss
+    on both sides, and the search keeps alpha = 0."""
+    _, X, W = synth.make_layer(1, 0, n_tokens=n_tokens, out_features=64)
+    _say(f"non-finite saliency {kind}, {n_tokens} tokens")
     sal_h = O.act_stats(X).copy()
-    sal_h[3] = np.nan
-    sal_h[200] = np.inf
+    if kind in ("nan", "both"):
+        sal_h[3] = np.nan
+    if kind in ("inf", "both"):
+        sal_h[200] = np.inf
     res = awq.awq_search_layer(dev(X), dev(W), dev(sal_h))
     torch.cuda.synchronize()
     ref = O.search_layer(X, W, sal_h)
