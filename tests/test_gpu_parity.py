@@ -318,6 +318,26 @@ def test_search_degenerate_inputs(awq):
     assert err.value.code == awq._lib.AWQ_ERR_NONFINITE
 
 
+def test_search_degenerate_inputs_contraction_path(awq):
+    """The same degenerate inputs on the contraction path (1100 tokens): all-zero
+    activations give zero losses and index 0; a NaN weight makes every grid
+    point's weight error NaN in its group, so no loss is finite: index -1 and
+    s_best all NaN."""
+    rng = np.random.default_rng(1)
+    W = (rng.standard_normal((40, 256)) * 0.02).astype(np.float16)
+    _, _, sal, res = run_layer(awq, np.zeros((1100, 256), np.float16), W)
+    assert res.plan.tile_out == 256
+    assert np.all(host(res.losses) == 0) and int(host(res.best_idx)[0]) == 0
+    Wn = W.copy()
+    Wn[7, 130] = np.float16(np.nan)
+    X = (rng.standard_normal((1100, 256))).astype(np.float16)
+    _, _, sal, res = run_layer(awq, X, Wn)
+    assert res.plan.tile_out == 256
+    assert np.all(np.isnan(host(res.losses)))
+    assert int(host(res.best_idx)[0]) == -1
+    assert np.all(np.isnan(host(res.s_best)))
+
+
 @pytest.mark.parametrize("n,k", [(64, 512), (9000, 64), (4096, 2048)])
 def test_stats_non_finite(awq, n, k):
     """NaN and infinities in X: a channel holding a NaN gets saliency NaN, one
