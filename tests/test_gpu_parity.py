@@ -803,10 +803,15 @@ def test_variant_split_last_round(awq, n, k, o, group, w_bit, zp):
     check_best(int(host(res.best_idx)[0]), ref.losses)
 
 
+@pytest.mark.parametrize("cfg_layer", [(2, 0), (5, 1)])
 @pytest.mark.parametrize("group,w_bit,zp", [(64, 3, True), (32, 4, False)])
-def test_variant_full_size_sampled_tiles(awq, group, w_bit, zp):
-    spec, X, W = synth.make_layer(2, 0)
-    _say(f"variant full size group {group} w_bit {w_bit} zero_point {zp}")
+def test_variant_full_size_sampled_tiles(awq, group, w_bit, zp, cfg_layer):
+    """Quantizer variants on a full-size layer of each grid path: the 7B q_proj
+    (512 tokens, fused kernels) and the 13B o_proj (4096 tokens, weight error
+    produced and contracted); per-tile partial sums of sampled tiles against
+    the oracle's."""
+    spec, X, W = synth.make_layer(*cfg_layer)
+    _say(f"variant full size {spec.name} group {group} w_bit {w_bit} zero_point {zp}")
     cfg = awq.default_config(group_size=group, w_bit=w_bit, zero_point=zp)
     Xd, Wd = dev(X), dev(W)
     sal = awq.awq_act_stats(Xd)
