@@ -219,13 +219,22 @@ def test_group_params_bit_exact(awq, n, k, o):
         assert np.array_equal(got[..., 3], np.float32(15) - zero), i
 
 
-def test_search_is_deterministic(awq):
-    _, X, W = synth.make_layer(3, n_tokens=256, out_features=512)
+@pytest.mark.parametrize("n_tokens", [256, 1100])
+def test_search_is_deterministic(awq, n_tokens):
+    """Three runs of the whole path are bitwise identical (a race check as
+    well): saliency, all losses, the choice, s_best and the packed layer, on
+    the fused path (256 tokens) and the contraction path (1100 tokens)."""
+    _, X, W = synth.make_layer(3, n_tokens=n_tokens, out_features=512)
     Xd, Wd = dev(X), dev(W)
-    sal = awq.awq_act_stats(Xd)
-    a = host(awq.awq_search_layer(Xd, Wd, sal).losses)
-    b = host(awq.awq_search_layer(Xd, Wd, sal).losses)
-    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+    runs = []
+    for _ in range(3):
+        sal = awq.awq_act_stats(Xd)
+        res = awq.awq_search_layer(Xd, Wd, sal)
+        qw, st, zr = awq.awq_pack(Wd, res.s_best)
+        runs.append([host(t) for t in (sal, res.losses, res.best_idx, res.s_best, qw, st, zr)])
+    for other in runs[1:]:
+        for x, y in zip(runs[0], other):
+            assert x.tobytes() == y.tobytes()
 
 
 def test_search_on_side_stream(awq):
