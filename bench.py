@@ -627,6 +627,7 @@ def main():
         kernels[spec.name] = {
             "shape": [spec.n_tokens, spec.in_features, spec.out_features],
             "best_idx": int(L["best"].item()),
+            "losses": [float(v) for v in L["losses"].cpu().tolist()],
             "ms": {nm: round(per[nm][li], 5) for nm in names},
             "ms_median": {nm: round(med(samples[nm][li]), 5) for nm in names},
             "ms_min": {nm: round(min(samples[nm][li]), 5) for nm in names},
