@@ -233,6 +233,23 @@ def test_select_top_validation(lib):
         == _lib.AWQ_ERR_INVALID_ARG
 
 
+def test_bench_cpu_baseline_fields():
+    # the oracle baseline of the benchmark line, on the small configuration:
+    # the rate over a bounded sample, the threads it used and what it sampled
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_for_cpu", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    r = bench.cpu_baseline(1, 0.5)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert r["host"]["affinity_cores"] >= 1 and r["host"]["blas_threads"] >= 1
+    assert [x["layer"] for x in r["per_layer"]] == ["linear"]
+    assert set(r["seconds"]) == {"stats", "search", "pack"}
+    assert "single_linear_in512_out512_tok128" in r["sample"]
+
+
 def test_bench_refuses_more_than_one_gpu():
     # the path runs on one GPU: a multi-GPU request exits with a message
     # before any device work
