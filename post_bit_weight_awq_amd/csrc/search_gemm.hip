@@ -24,13 +24,15 @@
 // r stored at p ^ (r & 7), so the fragment reads hit every bank once), one
 // barrier per step.  The weight-error tile has two LDS stages and is loaded
 // for step s + 1 at the start of step s; the activation tile has three and is
-// loaded for step s + 2 at the end of step s, after the MFMAs are issued and
-// before the barrier, where a wavefront would otherwise wait (160 KB of LDS).
-// The load instructions stall the wavefront that issues them; moving half of
-// them out of the step's start ran 0.5-2.6 % faster on the 13B shapes, where
-// a third activation stage loaded at the start lost 3-5 %.  A step reads both
-// 32-column halves' fragments first, then issues their 64 MFMAs.  Rows past
-// the last token or
+// loaded for step s + 2 in the middle of step s, between the MFMAs of its two
+// 32-column halves (160 KB of LDS).  The load instructions stall the
+// wavefront that issues them; with half of them out of the step's start the
+// kernel ran 2-3 % faster on the 13B shapes than with them after all the
+// MFMAs, and that 0.5-2.6 % faster than with all loads at the start (a third
+// activation stage loaded at the start lost 3-5 %).  The gain depends on the
+// exact order the compiler emits: the loads sit between two separate MFMA
+// loops, pinned by scheduling barriers.  A step reads both halves' fragments
+// first, then issues the MFMAs.  Rows past the last token or
 // output re-read the last row and are masked in the epilogue.  Each tile
 // writes its sum of squares (fp32 per lane, fp64 across the block) to its
 // grid point's partial slot.  Block order: the 32 blocks an XCD holds at a
@@ -133,22 +135,24 @@ k_grid_gemm(const _Float16* __restrict__ X, const _Float16* __restrict__ dW,
 #pragma unroll
       for (int n = 0; n < NT; ++n)
         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0[m], b0[n], acc[m][n], 0, 0, 0);
+    // the activation stage of step s + 2 also last held step s - 1; its loads
+    // go out between the two halves' MFMAs (the scheduling barriers keep them
+    // there)
+    const bool more = s + 2 < nk;
+    if (more) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int n = 0; n < NT; ++n)
         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1[m], b1[n], acc[m][n], 0, 0, 0);
-    // the activation stage of step s + 2 also last held step s - 1; its loads
-    // go out after this step's MFMAs (the scheduling barrier keeps them there)
-    const bool more = s + 2 < nk;
-    if (more) {
-      __builtin_amdgcn_sched_barrier(0);
-      load_x(s + 2);
-    }
     // step s + 1's tiles have landed (this wavefront's loads: the weight error
-    // issued this step, the activations last step; the activation loads just
-    // issued, the last 4, may stay in flight), and no wavefront still reads
-    // this step's stages (the barrier)
+    // issued this step, the activations last step; this step's activation
+    // loads, the last 4 issued, may stay in flight), and no wavefront still
+    // reads this step's stages (the barrier)
     if (more)
       __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
     else
