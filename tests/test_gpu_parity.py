@@ -302,6 +302,7 @@ def test_search_grid_stage_repeated(awq):
         assert np.array_equal(host(again.losses).view(np.uint64), first.view(np.uint64))
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered:RuntimeWarning")
 def test_search_degenerate_inputs(awq):
     # all-zero activations: saliency 0 is floored, every loss is 0, the first wins
     X = np.zeros((16, 256), np.float16)
@@ -327,6 +328,7 @@ def test_search_degenerate_inputs(awq):
     assert err.value.code == awq._lib.AWQ_ERR_NONFINITE
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered:RuntimeWarning")
 def test_search_degenerate_inputs_contraction_path(awq):
     """The same degenerate inputs on the contraction path (1100 tokens): all-zero
     activations give zero losses and index 0; a NaN weight makes every grid
@@ -368,6 +370,7 @@ def test_stats_non_finite(awq, n, k):
     assert np.array_equal(sal[fin].view(np.uint32), ref[fin].view(np.uint32))
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered:RuntimeWarning")
 @pytest.mark.parametrize("n_tokens", [64, 1100])
 @pytest.mark.parametrize("kind", ["nan", "inf", "both"])
 def test_search_non_finite_saliency(awq, n_tokens, kind):

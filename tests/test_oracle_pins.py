@@ -693,6 +693,7 @@ def test_w4a16_abs_matmul_matches_exact_rationals_and_bounds_the_product():
                                       "stats_nan_ignored", "no_unscale", "loss_over_tokens_only",
                                       "argmin_last", "stats_over_features", "no_floor",
                                       "pow_in_binary32"])
+@pytest.mark.filterwarnings("ignore:divide by zero encountered:RuntimeWarning")
 def test_planted_mistakes_fail_a_pin(mutation, monkeypatch):
     """Each plausible slip in the oracle trips at least one pin above."""
     if mutation == "no_unscale":
