@@ -202,13 +202,16 @@ def load_calib():
     lib.awq_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.awq_calib_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                                    ctypes.c_void_p]
+    lib.awq_calib_read_oneshot.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_void_p]
     return lib
 
 
 def cold_measurements(awq, cfg, layers, calib):
     """Stats and pack with the 256 MB last-level cache (MALL) cleared first by a
-    512 MiB streaming read, plus the same streaming read of X as a plain-read
-    reference, and an MFMA-only loop as the measured MFMA peak."""
+    512 MiB streaming read; as plain-read references, the fastest read measured
+    here (one shot per block, nontemporal loads) of X and of W after the same
+    clear; and an MFMA-only loop as the measured MFMA peak."""
     import torch
     stream = torch.cuda.current_stream().cuda_stream
     flush = torch.zeros(1 << 29, dtype=torch.uint8, device="cuda")
@@ -241,10 +244,10 @@ def cold_measurements(awq, cfg, layers, calib):
         ms_pack = timed(lambda: awq.awq_pack(L["W"], L["s_best"], cfg, qweight=L["qw"],
                                              step=L["st"], zero=L["zr"]))
         wb = L["W"].numel() * 2
-        ms_read = timed(lambda: calib.awq_calib_read(L["X"].data_ptr(), xb, sink.data_ptr(),
-                                                     4096, stream))
-        ms_read_w = timed(lambda: calib.awq_calib_read(L["W"].data_ptr(), wb, sink.data_ptr(),
-                                                       4096, stream))
+        ms_read = timed(lambda: calib.awq_calib_read_oneshot(L["X"].data_ptr(), xb,
+                                                             sink.data_ptr(), stream))
+        ms_read_w = timed(lambda: calib.awq_calib_read_oneshot(L["W"].data_ptr(), wb,
+                                                               sink.data_ptr(), stream))
         res[spec.name] = {"stats_gbs_cold": round(stats_bytes(spec) / (ms_stats * 1e-3) / 1e9, 1),
                           "pack_gbs_cold": round(pack_bytes(spec, cfg.group_size) /
                                                  (ms_pack * 1e-3) / 1e9, 1),
@@ -259,11 +262,11 @@ def cold_measurements(awq, cfg, layers, calib):
                                    for L in layers]),
         "pack_ms": timed(lambda: [awq.awq_pack(L["W"], L["s_best"], cfg, qweight=L["qw"],
                                                step=L["st"], zero=L["zr"]) for L in layers]),
-        "plain_read_of_X_ms": timed(lambda: [calib.awq_calib_read(
-            L["X"].data_ptr(), L["X"].numel() * 2, sink.data_ptr(), 4096, stream)
+        "plain_read_of_X_ms": timed(lambda: [calib.awq_calib_read_oneshot(
+            L["X"].data_ptr(), L["X"].numel() * 2, sink.data_ptr(), stream)
             for L in layers]),
-        "plain_read_of_W_ms": timed(lambda: [calib.awq_calib_read(
-            L["W"].data_ptr(), L["W"].numel() * 2, sink.data_ptr(), 4096, stream)
+        "plain_read_of_W_ms": timed(lambda: [calib.awq_calib_read_oneshot(
+            L["W"].data_ptr(), L["W"].numel() * 2, sink.data_ptr(), stream)
             for L in layers]),
     }
     del flush
@@ -357,8 +360,9 @@ def decode_bench(tokens, reps):
         per = {}
         for L, x, y in zip(layers, xs, ys):
             ms = median_ms(lambda: awq.awq_w4a16_matmul(x, L["qw"], L["st"], L["zr"], out=y))
-            rd = median_ms(lambda: calib.awq_calib_read(L["qw"].data_ptr(), L["qw"].numel() * 4,
-                                                        sink.data_ptr(), 4096, stream))
+            rd = median_ms(lambda: calib.awq_calib_read_oneshot(L["qw"].data_ptr(),
+                                                                L["qw"].numel() * 4,
+                                                                sink.data_ptr(), stream))
             per[L["name"]] = {"shape": [m, L["k"], L["o"]], "us": round(ms * 1e3, 2),
                               "gbs": round(layer_bytes(L, m) / (ms * 1e-3) / 1e9, 1),
                               "plain_read_of_codes_gbs": round(L["qw"].numel() * 4 /

@@ -6,7 +6,7 @@
 // HBM-bound column reduction.  Each lane owns 8 consecutive columns and reads
 // them with one 16-byte load per token row, so a wavefront reads 1 KiB of a row
 // contiguously.  The block's four wavefronts take interleaved rows of one row
-// chunk, eight rows in flight per lane.  |x| of an fp16 value is an integer
+// chunk, sixteen rows in flight per lane.  |x| of an fp16 value is an integer
 // multiple of 2^-24 below 2^16, so the per-lane binary64 sums are exact (at
 // most 8192 rows per chunk); the block's column totals are stored as 64-bit
 // integers in units of 2^-24, one row of partials per chunk.  A second kernel
@@ -57,13 +57,28 @@ k_act_stats(const uint4* __restrict__ X, int64_t n_tokens, int64_t in_features,
   if (col < in_features) {
     const uint4* p = X + r0 * row_vecs + col / 8;
     int64_t r = r0 + wave;
-    // eight rows in flight per lane
-    for (; r + 28 < r1; r += 32) {
-      uint4 v[8];
+    // sixteen rows in flight per lane: a 64-row chunk is one round of loads
+    for (; r + 60 < r1; r += 64) {
+      uint4 v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = p[(r - r0 + 4 * u) * row_vecs];
+      for (int u = 0; u < 16; ++u) v[u] = p[(r - r0 + 4 * u) * row_vecs];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          s[2 * j] += (double)fabsf(f16_lo(w[j]));
+          s[2 * j + 1] += (double)fabsf(f16_hi(w[j]));
+        }
+      }
+    }
+    // a ragged last chunk: four rows in flight, then one
+    for (; r + 12 < r1; r += 16) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = p[(r - r0 + 4 * u) * row_vecs];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -204,14 +219,14 @@ k_act_stats_1p(const uint4* __restrict__ X, int64_t n_tokens, int64_t in_feature
 StatsPlan stats_plan(int64_t n_tokens, int64_t in_features) {
   StatsPlan p;
   p.col_blocks = (in_features + kStatsCols - 1) / kStatsCols;
-  // about four blocks per compute unit, each streaming at least 64 rows (a
-  // multiple of 32: eight rows per wavefront per batch)
+  // about four blocks per compute unit, each streaming a multiple of 64 rows
+  // (sixteen rows per wavefront per round of loads)
   const int64_t want = (1024 + p.col_blocks - 1) / p.col_blocks;
   const int64_t max_chunks = (n_tokens + 63) / 64;
   p.row_chunks = want < max_chunks ? want : max_chunks;
   if (p.row_chunks < 1) p.row_chunks = 1;
   p.rows_per_chunk = (n_tokens + p.row_chunks - 1) / p.row_chunks;
-  p.rows_per_chunk = (p.rows_per_chunk + 31) / 32 * 32;
+  p.rows_per_chunk = (p.rows_per_chunk + 63) / 64 * 64;
   if (p.rows_per_chunk > 8192) {  // keep the per-lane binary64 sums exact
     p.rows_per_chunk = 8192;
   }

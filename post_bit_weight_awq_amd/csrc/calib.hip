@@ -63,6 +63,29 @@ k_read_stream(const uint4* __restrict__ x, int64_t n16, uint32_t* __restrict__ o
   if (acc == 0x9e3779b9u) out[0] = acc;
 }
 
+// The fastest plain read measured here: one shot per block (each block reads
+// 256 x 8 contiguous 16-byte pieces, all eight loads of a lane in flight at
+// once) with nontemporal loads.  On a 283 MB buffer after a last-level-cache
+// clear it moved 6.3 TB/s, against 5.2 TB/s for the grid-strided read above.
+constexpr int kOneShotPieces = 8;
+__global__ void __launch_bounds__(256)
+k_read_oneshot(const uint4* __restrict__ x, int64_t n16, uint32_t* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * 256 * kOneShotPieces + threadIdx.x;
+  uint4 v[kOneShotPieces];
+#pragma unroll
+  for (int u = 0; u < kOneShotPieces; ++u) {
+    const int64_t i = base + u * 256 < n16 ? base + u * 256 : n16 - 1;
+    v[u].x = __builtin_nontemporal_load(&x[i].x);
+    v[u].y = __builtin_nontemporal_load(&x[i].y);
+    v[u].z = __builtin_nontemporal_load(&x[i].z);
+    v[u].w = __builtin_nontemporal_load(&x[i].w);
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < kOneShotPieces; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  if (acc == 0x9e3779b9u) out[0] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +107,17 @@ int awq_calib_read(const void* buf, int64_t bytes, uint32_t* out, int n_blocks, 
     return -1;
   hipLaunchKernelGGL(k_read_stream, dim3(n_blocks), dim3(256), 0, (hipStream_t)stream,
                      (const uint4*)buf, bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Reads `bytes` (a multiple of 16, 16-byte aligned) of device memory once with
+// k_read_oneshot.  out: one uint32 of device memory (written only by chance).
+// Returns 0, -1, or -4.
+int awq_calib_read_oneshot(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  if (!buf || !out || bytes <= 0 || bytes % 16 != 0 || ((uintptr_t)buf & 15)) return -1;
+  const int64_t n16 = bytes / 16, per_block = 256 * kOneShotPieces;
+  hipLaunchKernelGGL(k_read_oneshot, dim3((unsigned)((n16 + per_block - 1) / per_block)), dim3(256),
+                     0, (hipStream_t)stream, (const uint4*)buf, n16, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
