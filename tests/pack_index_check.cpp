@@ -115,9 +115,10 @@ static void enumerate(int64_t K, int64_t OUT, int G) {
 
 int main() {
   int shapes = 0;
-  const int64_t Ks[] = {128, 256, 384, 512, 640, 1280, 4096, 5120, 10368, 11008, 13824, 27648,
-                        65536, 1 << 20};
-  const int64_t OUTs[] = {1, 2, 3, 7, 64, 300, 1000, 4096, 5120, 12288, 27648, 65537, 1 << 20};
+  const int64_t Ks[] = {128, 256, 384, 512, 640, 1024, 1280, 4096, 5120, 10368, 11008, 13824,
+                        27648, 65536, 1 << 20};
+  const int64_t OUTs[] = {1, 2, 3, 7, 48, 64, 77, 200, 300, 513, 1000, 4096, 5120, 12288, 27648,
+                          65537, 1 << 20};
   for (int G : {32, 64, 128})
     for (int64_t K : Ks)
       for (int64_t OUT : OUTs) {

@@ -152,6 +152,46 @@ def test_pack_edge_groups(awq):
     check_pack(qw, st, zr, ref, "edge groups")
 
 
+# The pack kernel's sweep mapping: one group per row, a group count per row
+# that is odd or coprime to the teams per wavefront, single and ragged
+# sweeps, and the three group sizes (teams of 1, 2 and 4 lanes).
+PACK_SWEEP = [(1, 128, 128), (3, 10368, 128), (77, 384, 32), (1000, 640, 64), (2, 13824, 128),
+              (513, 1280, 32)]
+
+
+@pytest.mark.parametrize("o,k,group", PACK_SWEEP)
+def test_pack_sweep_shapes(awq, o, k, group):
+    _say(f"pack sweep shape {o}x{k} group {group}")
+    rng = np.random.default_rng(7 * o + k)
+    W = (rng.standard_normal((o, k)) * 0.02).astype(np.float16)
+    s = rng.uniform(0.25, 4.0, k).astype(np.float32)
+    cfg = awq.default_config(group_size=group)
+    qw, st, zr = (host(t) for t in awq.awq_pack(dev(W), dev(s), cfg))
+    check_pack(qw, st, zr, O.pack(W, s, group), f"{o}x{k} group {group}")
+
+
+@pytest.mark.parametrize("zp", [True, False])
+def test_pack_groups_far_from_zero(awq, zp):
+    """Narrow groups far from zero (zero points of a few hundred to about ten
+    thousand, on both sides of the |z| <= 2048 bound under which the kernel
+    moves the zero point out of the clamp), and near zero."""
+    _say(f"pack groups far from zero, zero_point {zp}")
+    rng = np.random.default_rng(11)
+    k = 1024
+    rows = [off + rng.uniform(-hw, hw, (8, k))
+            for off, hw in ((40.0, 0.04), (100.0, 0.35), (-3.0, 0.03), (1000.0, 0.25),
+                            (-2000.0, 0.5), (0.0, 0.02))]
+    W = np.concatenate(rows).astype(np.float16)
+    s = np.ones(k, dtype=np.float32)
+    cfg = awq.default_config(zero_point=zp)
+    qw, st, zr = (host(t) for t in awq.awq_pack(dev(W), dev(s), cfg))
+    ref = O.pack(W, s, zero_point=zp)
+    if zp:
+        z = np.abs(ref.zero16.astype(np.float64))
+        assert (z > 2048).any() and ((z > 16) & (z <= 2048)).any()
+    check_pack(qw, st, zr, ref, f"far from zero, zero_point {zp}")
+
+
 # ----------------------------------------------- search: oracle-sized cases
 SEARCH_SMALL = [
     ("cfg1", dict(config=1)),
