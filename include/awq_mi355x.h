@@ -129,7 +129,7 @@ int awq_act_stats(const void* X, int64_t n_tokens, int64_t in_features, float* s
  * call on a device).  Shapes whose partials exceed it are rejected on the
  * host with AWQ_ERR_WORKSPACE before anything is enqueued: shapes with
  * n_tokens <= 8192 and n_tokens * in_features <= 2^22 need none, and the
- * rest need (row chunks) x in_features x 8 bytes, e.g. 3.5 MiB for
+ * rest need (row chunks) x in_features x 8 bytes, e.g. 3.4 MiB for
  * 4096 x 13824.  Every call on one GPU shares that GPU's array (each call
  * writes all it reads, so nothing carries over), so calls that overlap on
  * one GPU (different streams, or threads) race: serialize them. */
