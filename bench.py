@@ -21,8 +21,9 @@ printed on stdout:
                committed rocprofv3 counter summary; stats and pack against the
                HBM peak and a cold plain read of the same input
   kernels      per-stage times, TFLOP/s and GB/s, and stats and pack timed cold
-               (last-level cache cleared first) beside a plain streaming read
-               of X and of W
+               (last-level cache cleared first) beside the fastest plain read
+               measured here (one shot per block, nontemporal loads) of X and
+               of W
   measured_peaks  an MFMA-only loop (libawq_calib.so), for comparison with the
                published peak
   cpu_baseline the CPU oracle on a bounded sample of the same workload
